@@ -1,0 +1,212 @@
+"""Benchmark: one context-parallel rank's share of exact causal attention on
+one MI355X, through the C ABI.
+
+A step is one pass of the hot path over the rank's share: every KV block, in
+the seeded arrival order, folded into the (O, LSE) state by cpattn_partial
+(the LSE merge runs in the kernel's epilogue). Inputs and positions are
+resident in HBM before timing starts.
+
+Default workload: 65536 tokens zig-zag split over cp = 8, rank 1 — 8192 local
+queries x 32 heads, head_dim 128, bf16, against 8 KV blocks of 8192 tokens.
+
+Prints ONE JSON line. value = causal-effective TFLOP/s = 4 * d * (visible
+(query, key, head) triples) / time. roofline: the partial-attention kernel's
+algorithmic FLOPs per launch over its mean launch duration (HIP events on its
+stream) against MI355X's dense bf16 MFMA peak. cpu_baseline: the fp64 oracle
+on a bounded sample of the same rows, timed on the host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "causal-effective attention TFLOPS per rank share (bf16) + % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks (bf16; fp32 matrix)
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(q_pos, k_pos_blocks, q_start=None):
+    """Visible (query, key) pairs per block (per head), by counting on sorted positions."""
+    out = []
+    for kp in k_pos_blocks:
+        hi = np.searchsorted(kp, q_pos, side="right").astype(np.int64)
+        lo = 0 if q_start is None else np.searchsorted(kp, q_start, side="left").astype(np.int64)
+        out.append(int(np.sum(hi - lo)))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c1", help="c0..c4 (default c1, the headline configuration)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of this build "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_long_sequence_amd as cp
+    from context_long_sequence_amd.share import share_from_workload
+    from synth import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    cp.load_library()  # fails loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    log("workload %s: %s" % (wl.name, wl.description))
+    t0 = time.time()
+    share = share_from_workload(wl)
+    torch.cuda.synchronize()
+    log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
+    order = [int(b) for b in wl.arrival()]
+
+    qs = None
+    if share.cu_host is not None:
+        cu = share.cu_host
+        qs = cu[np.searchsorted(cu, share.q_pos_host, side="right") - 1]
+    pairs = visible_pairs(share.q_pos_host, share.k_pos_host, qs)
+    flops_blocks = [4.0 * wl.d * wl.hq * p for p in pairs]
+    step_flops = sum(flops_blocks)
+
+    for _ in range(args.warmup):
+        share.step(order)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; one event pair per kernel launch, on the launch stream
+    stream = torch.cuda.current_stream()
+    n_launch = args.steps * len(order)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    t_wall = time.perf_counter()
+    n = 0
+    for _ in range(args.steps):
+        for idx, b in enumerate(order):
+            ev[2 * n].record(stream)
+            share.call_block(b, share.o, share.lse, accumulate=idx > 0)
+            ev[2 * n + 1].record(stream)
+            n += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    launch_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_launch)])
+    ms_per_step = total_ms / args.steps
+    tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    kernel_flops = step_flops * args.steps / n_launch
+    kernel_ms = float(launch_ms.mean())
+    achieved = kernel_flops / (kernel_ms * 1e-3) / 1e12
+    log("%.3f ms/step (wall %.3f ms/step), %.1f TFLOP/s, kernel mean %.3f ms/launch" %
+        (ms_per_step, t_wall * 1e3 / args.steps, tflops, kernel_ms))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.description,
+            "name": wl.name,
+            "seq_len": wl.S, "cp_size": wl.cp, "rank": wl.rank, "layout": wl.layout,
+            "local_queries": wl.lq, "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.d,
+            "kv_blocks": wl.n_blocks, "arrival_order": order, "global_batch": 1,
+            "parallelism": "one cp%d rank share on 1 GPU" % wl.cp,
+            "visible_pairs_per_head": int(sum(pairs)),
+            "causal_effective_flop_per_step": step_flops,
+        },
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {
+            "kernel": "partial_fwd_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "flop_per_launch": kernel_flops,
+            "mean_launch_ms": round(kernel_ms, 5),
+            "launches": n_launch,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, share, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, share, seconds):
+    """Time the fp64 oracle on a bounded sample of the same workload's rows,
+    and check the GPU output on that sample."""
+    import oracle
+    orc = oracle.get()
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    docs = wl.doc_lens()
+    qp, qst = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
+    kps = []
+    for b in range(wl.n_blocks):
+        if wl.block_kind == "rank_shares":
+            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
+        elif wl.block_kind == "chunks":
+            c = wl.S // wl.n_blocks
+            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
+        else:
+            kps.append(np.arange(wl.S, dtype=np.int32))
+    log("cpu baseline: loading inputs on the host")
+    q = wl.q()
+    k = np.concatenate([wl.kv_block(b, "k") for b in range(wl.n_blocks)])
+    v = np.concatenate([wl.kv_block(b, "v") for b in range(wl.n_blocks)])
+    kp = np.concatenate(kps)
+    qstart = qst if docs is not None else None
+    # calibrate: a small sample first, then scale to ~`seconds`
+    n = 32
+    while True:
+        rows, heads = wl.sample_pairs(n)
+        t = time.perf_counter()
+        o_ref, lse_ref, cnt = orc.attention(q, k, v, qp, kp, qstart, True, rows=rows, heads=heads, n_threads=threads)
+        dt = time.perf_counter() - t
+        if dt >= 0.5 * seconds or n >= wl.lq * wl.hq:
+            break
+        n = int(min(wl.lq * wl.hq, max(2 * n, n * seconds / max(dt, 1e-3))))
+    flops = 4.0 * wl.d * float(np.sum(cnt))
+    o = share.o.float().cpu().numpy()
+    lse = share.lse.cpu().numpy()
+    eo = float(np.max(np.abs(o[rows, heads] - o_ref)))
+    el = float(np.max(np.abs(lse[heads, rows] - lse_ref)))
+    log("cpu baseline: %d (row, head) pairs in %.1f s on %d threads; GPU vs oracle max|dO| %.2e max|dLSE| %.2e"
+        % (len(rows), dt, threads, eo, el))
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d sampled (query row, head) pairs of this workload against all its keys, fp64 two-pass "
+                  "softmax attention, %.1f s" % (len(rows), dt),
+        "seconds": round(dt, 3),
+        "gpu_vs_oracle_max_abs_err": {"o": eo, "lse": el},
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""Python binding of libcpattn.so: one context-parallel rank's exact blockwise
+attention on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/cpattn.h). PyTorch supplies device memory
+and the current stream. There is no fallback: if the library is missing or a
+call fails, a ``CpattnError`` is raised.
+
+Functions (same names as the C ABI):
+  cpattn_zigzag_index(total_len, cp_size, rank, layout, cu_seqlens=None)
+  cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0, accumulate=False)
+  cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_scale=0.0, accumulate=False)
+  cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
+
+Layouts: q, o [lq, hq, d]; k, v [lk, hkv, d]; lse [hq, lq] float32; positions
+int32 ascending. See include/cpattn.h for the full contract.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcpattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "cpattn.h")
+
+CPATTN_BF16, CPATTN_F32 = 0, 1
+LAYOUTS = {"contiguous": 0, "zigzag": 1, "striped": 2}
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSORTED", 5: "ERR_RANGE",
+          6: "ERR_ALIGN", 7: "ERR_ALIAS", 8: "ERR_HIP"}
+
+
+class CpattnError(RuntimeError):
+    """A non-OK status from the library (or the library is missing)."""
+
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libcpattn.so (built by context_long_sequence_amd/build.py); raise if absent."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise CpattnError(-1, "libcpattn.so not found at %s; run `python -m context_long_sequence_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    lib.cpattn_version.restype = ctypes.c_int
+    lib.cpattn_version.argtypes = []
+    lib.cpattn_last_error.restype = ctypes.c_char_p
+    lib.cpattn_last_error.argtypes = []
+    lib.cpattn_zigzag_index.restype = ctypes.c_int
+    lib.cpattn_zigzag_index.argtypes = [i64, i32, i32, ctypes.c_int, vp, i32, vp, vp]
+    lib.cpattn_partial.restype = ctypes.c_int
+    lib.cpattn_partial.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, i32, f32,
+                                   vp, ctypes.c_int, vp, i32, vp]
+    lib.cpattn_varlen_partial.restype = ctypes.c_int
+    lib.cpattn_varlen_partial.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32, f32,
+                                          vp, ctypes.c_int, vp, i32, vp]
+    lib.cpattn_merge_lse.restype = ctypes.c_int
+    lib.cpattn_merge_lse.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def header_functions(path=HEADER):
+    """Names of the functions declared in include/cpattn.h."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(cpattn_[a-z_]+)\s*\(", text, re.M)))
+
+
+def _check(lib, status):
+    if status != 0:
+        raise CpattnError(status, lib.cpattn_last_error().decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CPATTN_BF16
+    if t.dtype == torch.float32:
+        return CPATTN_F32
+    raise CpattnError(3, "tensor dtype %s is not bfloat16 or float32" % t.dtype)
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise CpattnError(1, "%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise CpattnError(2, "%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise CpattnError(3, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def cpattn_version():
+    return load_library().cpattn_version()
+
+
+def cpattn_zigzag_index(total_len, cp_size, rank, layout="zigzag", cu_seqlens=None):
+    """Global positions of `rank`'s tokens (and each token's document start), as int32 numpy arrays."""
+    lib = load_library()
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    n = total_len // cp_size if cp_size > 0 else 0
+    pos = np.zeros(max(n, 1), np.int32)
+    start = np.zeros(max(n, 1), np.int32)
+    cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, np.int32)
+    st = lib.cpattn_zigzag_index(int(total_len), int(cp_size), int(rank), lay,
+                                 None if cu is None else cu.ctypes.data,
+                                 0 if cu is None else len(cu) - 1, pos.ctypes.data, start.ctypes.data)
+    _check(lib, st)
+    return pos[:n], start[:n]
+
+
+def _shapes(q, k, o, lse):
+    if q.dim() != 3 or k.dim() != 3 or o.dim() != 3 or lse.dim() != 2:
+        raise CpattnError(2, "q, k, v, o must be 3-D [tokens, heads, head_dim] and lse 2-D [heads, tokens]")
+    lq, hq, d = q.shape
+    lk, hkv, d2 = k.shape
+    if d2 != d or tuple(o.shape) != (lq, hq, d) or tuple(lse.shape) != (hq, lq):
+        raise CpattnError(2, "shape mismatch: q %s k %s o %s lse %s" % (tuple(q.shape), tuple(k.shape),
+                                                                        tuple(o.shape), tuple(lse.shape)))
+    return lq, lk, hq, hkv, d
+
+
+def cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0, accumulate=False, stream=None):
+    """Fold one KV block into (o, lse); see cpattn_partial in include/cpattn.h."""
+    import torch
+    lib = load_library()
+    lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
+    if tuple(v.shape) != tuple(k.shape):
+        raise CpattnError(2, "v must have k's shape")
+    st = lib.cpattn_partial(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq, lk, hq,
+                            hkv, d, _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
+                            int(bool(causal)), float(softmax_scale), _dev(o, "o"), _dtype_code(o),
+                            _dev(lse, "lse", torch.float32), int(bool(accumulate)), _stream(stream))
+    _check(lib, st)
+
+
+def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_scale=0.0, accumulate=False,
+                          stream=None):
+    """As cpattn_partial, causal within documents given by device cu_seqlens."""
+    import torch
+    lib = load_library()
+    lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
+    if tuple(v.shape) != tuple(k.shape):
+        raise CpattnError(2, "v must have k's shape")
+    st = lib.cpattn_varlen_partial(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq,
+                                   lk, hq, hkv, d, _dev(q_pos, "q_pos", torch.int32),
+                                   _dev(k_pos, "k_pos", torch.int32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                                   cu_seqlens.numel() - 1, float(softmax_scale), _dev(o, "o"), _dtype_code(o),
+                                   _dev(lse, "lse", torch.float32), int(bool(accumulate)), _stream(stream))
+    _check(lib, st)
+
+
+def cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part, stream=None):
+    """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
+    import torch
+    lib = load_library()
+    if o_acc.dim() != 3 or tuple(o_part.shape) != tuple(o_acc.shape) or o_part.dtype != o_acc.dtype:
+        raise CpattnError(2, "o_acc and o_part must be [lq, hq, d] of one dtype")
+    lq, hq, d = o_acc.shape
+    if tuple(lse_acc.shape) != (hq, lq) or tuple(lse_part.shape) != (hq, lq):
+        raise CpattnError(2, "lse tensors must be [hq, lq]")
+    st = lib.cpattn_merge_lse(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc", torch.float32), _dev(o_part, "o_part"),
+                              _dev(lse_part, "lse_part", torch.float32), _dtype_code(o_acc), lq, hq, d,
+                              _stream(stream))
+    _check(lib, st)
+
+
+__all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_merge_lse", "cpattn_version",
+           "CpattnError", "load_library", "header_functions"]

@@ -1,0 +1,235 @@
+// api.cpp — the C ABI declared in include/cpattn.h: argument validation
+// (always before any HIP call), the host-side index builder, and the kernel
+// launches. No allocation, no state kept between calls.
+#include "cpattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+cpattn_status fail(cpattn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+cpattn_status ok() {
+  g_err[0] = '\0';
+  return CPATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool validate_env() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("CPATTN_VALIDATE");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// Optional O(n) check that device positions ascend (synchronises `stream`).
+cpattn_status check_sorted_device(const int32_t* dptr, int64_t n, const char* name, hipStream_t stream) {
+  if (n <= 1) return CPATTN_OK;
+  std::vector<int32_t> h((size_t)n);
+  hipError_t e = hipMemcpyAsync(h.data(), dptr, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "reading %s for validation: %s", name, hipGetErrorString(e));
+  for (int64_t i = 1; i < n; ++i)
+    if (h[(size_t)i] < h[(size_t)i - 1])
+      return fail(CPATTN_ERR_UNSORTED, "%s is not ascending at index %lld", name, (long long)i);
+  return CPATTN_OK;
+}
+
+size_t dsize(cpattn_dtype t) { return t == CPATTN_BF16 ? 2 : 4; }
+
+cpattn_status check_partial_args(const void* q, const void* k, const void* v, cpattn_dtype in_dtype, int64_t lq,
+                                 int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                 const int32_t* k_pos, int32_t causal, void* o, cpattn_dtype o_dtype,
+                                 const float* lse, int32_t accumulate) {
+  // zero-sized operands may be NULL (an empty tensor has no storage)
+  if (lq != 0 && (!q || !o || !lse)) return fail(CPATTN_ERR_NULL, "q, o and lse must be non-NULL");
+  if (lk != 0 && (!k || !v)) return fail(CPATTN_ERR_NULL, "k and v must be non-NULL");
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_RANGE, "causal must be 0 or 1, got %d", causal);
+  if (accumulate != 0 && accumulate != 1) return fail(CPATTN_ERR_RANGE, "accumulate must be 0 or 1, got %d", accumulate);
+  if (causal && ((lq != 0 && !q_pos) || (lk != 0 && !k_pos)))
+    return fail(CPATTN_ERR_NULL, "q_pos and k_pos are required when causal");
+  if (in_dtype != CPATTN_BF16 && in_dtype != CPATTN_F32) return fail(CPATTN_ERR_DTYPE, "in_dtype %d unsupported", (int)in_dtype);
+  if (o_dtype != CPATTN_BF16 && o_dtype != CPATTN_F32) return fail(CPATTN_ERR_DTYPE, "o_dtype %d unsupported", (int)o_dtype);
+  if (in_dtype == CPATTN_F32 && o_dtype != CPATTN_F32)
+    return fail(CPATTN_ERR_DTYPE, "float32 inputs need a float32 output");
+  if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
+  if (hq < 1 || hkv < 1) return fail(CPATTN_ERR_SHAPE, "hq and hkv must be >= 1 (hq=%d hkv=%d)", hq, hkv);
+  if (hq % hkv) return fail(CPATTN_ERR_SHAPE, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
+  if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
+  if ((int64_t)hq * head_dim * lq >= (int64_t)1 << 40) return fail(CPATTN_ERR_SHAPE, "q is too large");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(CPATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || (q_pos && !aligned(q_pos, 4)) || (k_pos && !aligned(k_pos, 4)))
+    return fail(CPATTN_ERR_ALIGN, "lse and positions must be 4-byte aligned");
+  const size_t nq = (size_t)lq * hq * head_dim * dsize(in_dtype);
+  const size_t nk = (size_t)lk * hkv * head_dim * dsize(in_dtype);
+  const size_t no = (size_t)lq * hq * head_dim * dsize(o_dtype);
+  const size_t nl = (size_t)lq * hq * sizeof(float);
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nk) || overlaps(lse, nl, q, nq) ||
+      overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) || overlaps(o, no, lse, nl))
+    return fail(CPATTN_ERR_ALIAS, "outputs must not overlap inputs or each other");
+  return CPATTN_OK;
+}
+
+cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpattn_dtype in_dtype, int64_t lq,
+                              int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                              const int32_t* k_pos, const int32_t* cu_seqlens, int32_t n_seqs, int32_t causal,
+                              float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse, int32_t accumulate,
+                              void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_env() && causal) {
+    cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
+    if (st == CPATTN_OK) st = check_sorted_device(k_pos, lk, "k_pos", s);
+    if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
+    if (st != CPATTN_OK) return st;
+  }
+  if (lq == 0) return ok();
+  cpattn::PartialParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_pos = q_pos; p.k_pos = k_pos; p.cu_seqlens = cu_seqlens; p.n_seqs = n_seqs;
+  p.lq = lq; p.lk = lk; p.hq = hq; p.hkv = hkv;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal; p.accumulate = accumulate;
+  hipError_t e = cpattn::launch_partial(p, in_dtype == CPATTN_BF16, o_dtype == CPATTN_BF16, head_dim,
+                                        cu_seqlens != nullptr, s);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpattn_version(void) { return 100; }
+
+const char* cpattn_last_error(void) { return g_err; }
+
+cpattn_status cpattn_zigzag_index(int64_t total_len, int32_t cp_size, int32_t rank, cpattn_layout layout,
+                                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t* out_pos,
+                                  int32_t* out_seq_start) {
+  if (!out_pos) return fail(CPATTN_ERR_NULL, "out_pos must be non-NULL");
+  if (cp_size < 1) return fail(CPATTN_ERR_RANGE, "cp_size must be >= 1, got %d", cp_size);
+  if (rank < 0 || rank >= cp_size) return fail(CPATTN_ERR_RANGE, "rank %d outside [0, %d)", rank, cp_size);
+  if (layout != CPATTN_CONTIGUOUS && layout != CPATTN_ZIGZAG && layout != CPATTN_STRIPED)
+    return fail(CPATTN_ERR_RANGE, "unknown layout %d", (int)layout);
+  if (total_len < 0 || total_len >= ((int64_t)1 << 31)) return fail(CPATTN_ERR_SHAPE, "total_len must be in [0, 2^31)");
+  const int64_t unit = layout == CPATTN_ZIGZAG ? 2 * (int64_t)cp_size : cp_size;
+  // documents: [start_t, end_t); one document when cu_seqlens is NULL
+  int32_t nd = 1;
+  if (cu_seqlens) {
+    if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1 with cu_seqlens");
+    if (cu_seqlens[0] != 0) return fail(CPATTN_ERR_SHAPE, "cu_seqlens[0] must be 0");
+    if (cu_seqlens[n_seqs] != total_len)
+      return fail(CPATTN_ERR_SHAPE, "cu_seqlens[n_seqs] (%d) must equal total_len (%lld)", cu_seqlens[n_seqs],
+                  (long long)total_len);
+    for (int32_t t = 0; t < n_seqs; ++t) {
+      if (cu_seqlens[t + 1] < cu_seqlens[t]) return fail(CPATTN_ERR_UNSORTED, "cu_seqlens must ascend");
+      if ((cu_seqlens[t + 1] - cu_seqlens[t]) % unit)
+        return fail(CPATTN_ERR_SHAPE, "document %d length %d is not a multiple of %lld", t,
+                    cu_seqlens[t + 1] - cu_seqlens[t], (long long)unit);
+    }
+    nd = n_seqs;
+  } else if (total_len % unit) {
+    return fail(CPATTN_ERR_SHAPE, "total_len %lld is not a multiple of %lld", (long long)total_len, (long long)unit);
+  }
+  int64_t n = 0;
+  for (int32_t t = 0; t < nd; ++t) {
+    const int64_t s0 = cu_seqlens ? cu_seqlens[t] : 0;
+    const int64_t len = cu_seqlens ? (int64_t)cu_seqlens[t + 1] - s0 : total_len;
+    const int64_t per = len / cp_size;  // tokens of this document on each rank
+    for (int64_t u = 0; u < per; ++u) {
+      int64_t pos;
+      if (layout == CPATTN_CONTIGUOUS) {
+        pos = (int64_t)rank * per + u;
+      } else if (layout == CPATTN_STRIPED) {
+        pos = u * cp_size + rank;
+      } else {
+        const int64_t c = len / (2 * (int64_t)cp_size);  // zig-zag chunk length
+        pos = (u < c) ? (int64_t)rank * c + u : (int64_t)(2 * cp_size - 1 - rank) * c + (u - c);
+      }
+      out_pos[n] = (int32_t)(s0 + pos);
+      if (out_seq_start) out_seq_start[n] = (int32_t)s0;
+      ++n;
+    }
+  }
+  return ok();
+}
+
+cpattn_status cpattn_partial(const void* q, const void* k, const void* v, cpattn_dtype in_dtype, int64_t lq,
+                             int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                             const int32_t* k_pos, int32_t causal, float softmax_scale, void* o,
+                             cpattn_dtype o_dtype, float* lse, int32_t accumulate, void* stream) {
+  cpattn_status st = check_partial_args(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, causal, o,
+                                        o_dtype, lse, accumulate);
+  if (st != CPATTN_OK) return st;
+  if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
+  return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, nullptr, 0, causal,
+                         softmax_scale, o, o_dtype, lse, accumulate, stream);
+}
+
+cpattn_status cpattn_varlen_partial(const void* q, const void* k, const void* v, cpattn_dtype in_dtype, int64_t lq,
+                                    int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                    const int32_t* k_pos, const int32_t* cu_seqlens, int32_t n_seqs,
+                                    float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse,
+                                    int32_t accumulate, void* stream) {
+  cpattn_status st = check_partial_args(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, 1, o, o_dtype,
+                                        lse, accumulate);
+  if (st != CPATTN_OK) return st;
+  if (!cu_seqlens) return fail(CPATTN_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
+  return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, cu_seqlens, n_seqs, 1,
+                         softmax_scale, o, o_dtype, lse, accumulate, stream);
+}
+
+cpattn_status cpattn_merge_lse(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
+                               cpattn_dtype o_dtype, int64_t lq, int32_t hq, int32_t head_dim, void* stream) {
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(CPATTN_ERR_NULL, "all four buffers must be non-NULL");
+  if (o_dtype != CPATTN_BF16 && o_dtype != CPATTN_F32) return fail(CPATTN_ERR_DTYPE, "o_dtype %d unsupported", (int)o_dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
+  if (lq < 0 || hq < 1) return fail(CPATTN_ERR_SHAPE, "lq must be >= 0 and hq >= 1");
+  if (lq >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq must be < 2^31");
+  if (!aligned(o_acc, 16) || !aligned(o_part, 16)) return fail(CPATTN_ERR_ALIGN, "o buffers must be 16-byte aligned");
+  if (!aligned(lse_acc, 4) || !aligned(lse_part, 4)) return fail(CPATTN_ERR_ALIGN, "lse buffers must be 4-byte aligned");
+  const size_t no = (size_t)lq * hq * head_dim * dsize(o_dtype);
+  const size_t nl = (size_t)lq * hq * sizeof(float);
+  if (overlaps(o_acc, no, o_part, no) || overlaps(lse_acc, nl, lse_part, nl) || overlaps(o_acc, no, lse_acc, nl) ||
+      overlaps(o_acc, no, lse_part, nl) || overlaps(lse_acc, nl, o_part, no))
+    return fail(CPATTN_ERR_ALIAS, "o_part/lse_part must not overlap o_acc/lse_acc");
+  if (lq == 0) return ok();
+  hipError_t e = cpattn::launch_merge(o_acc, lse_acc, o_part, lse_part, o_dtype == CPATTN_BF16, lq, hq, head_dim,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// device_common.hpp — small device helpers shared by the gfx950 kernels:
+// vector types, position searches, the cross-half-wave exchange, and the
+// two-partial merge used both by the partial-attention epilogue and by the
+// standalone merge kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+#define CPATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// First index in the ascending array a[0, n) with a[idx] > x.
+__device__ __forceinline__ int64_t upper_bound_i32(const int32_t* a, int64_t n, int32_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// First index in the ascending array a[0, n) with a[idx] >= x.
+__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int32_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Start offset of the document holding global position p: the largest
+// cu_seqlens entry <= p (cu_seqlens is ascending, cu_seqlens[0] == 0).
+__device__ __forceinline__ int32_t doc_start(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
+  int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, p) - 1;
+  return cu_seqlens[idx < 0 ? 0 : idx];
+}
+
+// v_permlane32_swap exchanges the upper half-wave of its first operand with
+// the lower half-wave of its second. Passing the same value twice leaves, in
+// every lane, one result equal to the lane's own value and the other equal to
+// the value of lane ^ 32, so a symmetric reduction needs no lane test.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Merge weights of two partial results with natural-log normalisers la, lb:
+// L = ln(e^la + e^lb), wa = e^(la-L), wb = e^(lb-L). A -inf side gets weight
+// exactly 0 and the other side exactly 1; both -inf gives L = -inf, w = 0.
+__device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb, float& L) {
+  float mx = fmaxf(la, lb);
+  if (mx == neg_inf()) {
+    wa = 0.f; wb = 0.f; L = neg_inf();
+    return;
+  }
+  float ea = __builtin_amdgcn_exp2f((la - mx) * kLog2e);   // one of ea, eb is exactly 1
+  float eb = __builtin_amdgcn_exp2f((lb - mx) * kLog2e);
+  float s = ea + eb;
+  float inv = 1.0f / s;
+  L = mx + __builtin_amdgcn_logf(s) * kLn2;
+  wa = ea * inv;
+  wb = eb * inv;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 bit pattern (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+}  // namespace cpattn

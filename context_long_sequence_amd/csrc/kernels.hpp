@@ -1,0 +1,35 @@
+// kernels.hpp — host-visible launch interface between the C-ABI layer
+// (api.cpp) and the gfx950 kernels. Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+struct PartialParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* q_pos;
+  const int32_t* k_pos;
+  const int32_t* cu_seqlens;
+  int32_t n_seqs;
+  int64_t lq, lk;
+  int32_t hq, hkv;
+  int32_t g_wg, r_wg;         // query heads / 32-row blocks per workgroup (set by launch_partial)
+  int32_t n_qtiles, n_hgroups, n_wg;
+  float scale_log2;           // softmax scale * log2(e)
+  int32_t causal, accumulate;
+};
+
+// Enqueue the partial-attention kernel; arguments are already validated.
+hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_dim, bool varlen, hipStream_t stream);
+
+// Enqueue the standalone merge (o_acc, lse_acc) <- merge(acc, part).
+hipError_t launch_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part, int out_bf16,
+                        int64_t lq, int32_t hq, int32_t head_dim, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,108 @@
+"""One rank's share of context-parallel attention: device-resident inputs and
+the per-step driver that feeds KV blocks to the library in arrival order.
+
+Orchestration only — every arithmetic step runs in the HIP kernels behind
+the C ABI. This is the loop of the FCP page ("从固定环到自由拓扑：FCP到底在解决
+什么", §3.3): each arriving block is folded into the rank's running
+(O, LSE) state, in whatever order the blocks arrive.
+"""
+import numpy as np
+
+from . import cpattn_merge_lse, cpattn_partial, cpattn_varlen_partial, cpattn_zigzag_index
+
+
+def bits_to_device(a, device="cuda"):
+    """numpy uint16 (bf16 bit patterns) or float32 array -> torch tensor on `device`."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def block_positions(S, cp, n_blocks, block_kind, layout, cu_seqlens=None):
+    """Global positions of every KV block's tokens, in block-id order (int32 numpy arrays)."""
+    if block_kind == "rank_shares":
+        return [cpattn_zigzag_index(S, cp, b, layout, cu_seqlens)[0] for b in range(n_blocks)]
+    if block_kind == "chunks":
+        c = S // n_blocks
+        return [np.arange(b * c, (b + 1) * c, dtype=np.int32) for b in range(n_blocks)]
+    if block_kind == "whole":
+        return [np.arange(S, dtype=np.int32)]
+    raise ValueError(block_kind)
+
+
+class RankShare:
+    """Device tensors of one rank's share and the step that runs every block.
+
+    q [lq, hq, d]; k_blocks / v_blocks: lists of [lk_b, hkv, d]; positions as
+    int32 device tensors; cu_seqlens (optional) as an int32 device tensor.
+    """
+
+    def __init__(self, q, k_blocks, v_blocks, q_pos, k_pos_blocks, cu_seqlens=None, causal=True, out_dtype=None):
+        import torch
+        self.q, self.k_blocks, self.v_blocks = q, k_blocks, v_blocks
+        self.q_pos, self.k_pos_blocks = q_pos, k_pos_blocks
+        self.cu_seqlens = cu_seqlens
+        self.causal = causal
+        lq, hq, d = q.shape
+        self.out_dtype = out_dtype or q.dtype
+        self.o = torch.empty((lq, hq, d), dtype=self.out_dtype, device=q.device)
+        self.lse = torch.empty((hq, lq), dtype=torch.float32, device=q.device)
+        self._o_part = None
+        self._lse_part = None
+
+    @property
+    def n_blocks(self):
+        return len(self.k_blocks)
+
+    def call_block(self, b, o, lse, accumulate):
+        if self.cu_seqlens is not None:
+            cpattn_varlen_partial(self.q, self.k_blocks[b], self.v_blocks[b], self.q_pos, self.k_pos_blocks[b],
+                                  self.cu_seqlens, o, lse, accumulate=accumulate)
+        else:
+            cpattn_partial(self.q, self.k_blocks[b], self.v_blocks[b], self.q_pos, self.k_pos_blocks[b], o, lse,
+                           causal=self.causal, accumulate=accumulate)
+
+    def step(self, order, mode="accumulate"):
+        """Fold every block, in `order`, into (self.o, self.lse) and return them.
+
+        mode 'accumulate': the kernel merges each block in its epilogue.
+        mode 'merge': each block is written as its own partial, then merged by
+        the standalone merge kernel.
+        """
+        import torch
+        order = list(order)
+        self.call_block(order[0], self.o, self.lse, accumulate=False)
+        if mode == "accumulate":
+            for b in order[1:]:
+                self.call_block(b, self.o, self.lse, accumulate=True)
+        elif mode == "merge":
+            if self._o_part is None:
+                self._o_part = torch.empty_like(self.o)
+                self._lse_part = torch.empty_like(self.lse)
+            for b in order[1:]:
+                self.call_block(b, self._o_part, self._lse_part, accumulate=False)
+                cpattn_merge_lse(self.o, self.lse, self._o_part, self._lse_part)
+        else:
+            raise ValueError(mode)
+        return self.o, self.lse
+
+
+def share_from_workload(wl, device="cuda", blocks=None):
+    """Build a RankShare for a synth.Workload: positions from the library's
+    index builder, tensors from the seeded generators."""
+    import torch
+    docs = wl.doc_lens()
+    cu = None if docs is None else np.concatenate([[0], np.cumsum(docs)]).astype(np.int32)
+    q_pos, _ = cpattn_zigzag_index(wl.S, wl.cp, wl.rank, wl.layout, cu)
+    kps = block_positions(wl.S, wl.cp, wl.n_blocks, wl.block_kind, wl.layout, cu)
+    blocks = range(wl.n_blocks) if blocks is None else blocks
+    kb = [bits_to_device(wl.kv_block(b, "k"), device) for b in blocks]
+    vb = [bits_to_device(wl.kv_block(b, "v"), device) for b in blocks]
+    kp = [torch.from_numpy(kps[b]).to(device) for b in blocks]
+    share = RankShare(bits_to_device(wl.q(), device), kb, vb, torch.from_numpy(q_pos).to(device), kp,
+                      None if cu is None else torch.from_numpy(cu).to(device))
+    share.q_pos_host = q_pos
+    share.k_pos_host = [kps[b] for b in blocks]
+    share.cu_host = cu
+    return share

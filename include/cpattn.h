@@ -1,0 +1,162 @@
+/*
+ * cpattn.h — C ABI of the MI355X (gfx950) library for one context-parallel
+ * rank's exact blockwise attention.
+ *
+ * The problem these calls solve is the one stated on the FCP page
+ * ("从固定环到自由拓扑：FCP到底在解决什么", §3.3): a rank keeps its local query
+ * shard, KV blocks of the other ranks arrive one at a time in an order the
+ * communication graph decides, and each arriving block is folded into the
+ * running softmax state so that the final result equals ordinary attention
+ * whatever the order. Masking is causal by GLOBAL token position (PCP page
+ * "大模型长序列显存优化：PCP与DCP序列并行实战指南", §3.5: positions stay global
+ * after the split; zig-zag page "大模型长上下文训练的挑战与突破", §4.2: a token
+ * sees only earlier tokens). Query heads may share KV heads (GQA) without
+ * copying them (Halo page "长上下文训练 256k 不难：Halo 上下文并行（CP + Ulysses
+ * 注意力）原理与实测", Ulysses section).
+ *
+ * Conventions shared by every call
+ *  - Q and O are [lq][hq][head_dim], K and V are [lk][hkv][head_dim], all
+ *    row-major and contiguous; LSE is [hq][lq] float32.
+ *  - Query head h reads KV head h / (hq / hkv).
+ *  - scores are scale * <q, k>; LSE is the natural log of the softmax
+ *    normaliser, LSE = max + ln(sum of exp(score - max)).
+ *  - A query row with no visible key in a call has O = 0 and LSE = -inf; a
+ *    merge gives such a partial zero weight, so no NaN is ever produced.
+ *  - Positions are int32, ascending within each array (the kernels find the
+ *    visible key range by binary search and rely on it).
+ *
+ * Ownership: the caller allocates and owns every buffer. Device pointers are
+ * plain HIP device allocations on the current device; host pointers are
+ * plain host memory. The library keeps no state between calls and allocates
+ * no device memory.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued.
+ * A non-OK status means nothing was enqueued; cpattn_last_error() returns a
+ * message for the calling thread. CPATTN_OK means the work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream); device-side faults
+ * surface at the caller's next synchronisation. With the environment variable
+ * CPATTN_VALIDATE=1 the calls also copy the position arrays to the host and
+ * check that they are ascending (this synchronises the stream).
+ *
+ * Calls are reentrant; the error text is thread-local.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_ERR_NULL = 1,      /* a required pointer is NULL */
+    CPATTN_ERR_SHAPE = 2,     /* sizes inconsistent, unsupported head_dim, or not divisible */
+    CPATTN_ERR_DTYPE = 3,     /* unsupported dtype or dtype combination */
+    CPATTN_ERR_UNSORTED = 4,  /* positions or offsets not ascending */
+    CPATTN_ERR_RANGE = 5,     /* rank, cp size, layout or flag out of range */
+    CPATTN_ERR_ALIGN = 6,     /* a pointer is misaligned (16 bytes for tensors, 4 for int32/float32 arrays) */
+    CPATTN_ERR_ALIAS = 7,     /* an output overlaps an input */
+    CPATTN_ERR_HIP = 8        /* a HIP runtime call failed; the message holds hipGetErrorString */
+} cpattn_status;
+
+typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
+
+typedef enum { CPATTN_CONTIGUOUS = 0, CPATTN_ZIGZAG = 1, CPATTN_STRIPED = 2 } cpattn_layout;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int cpattn_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *cpattn_last_error(void);
+
+/*
+ * Global positions of rank `rank`'s tokens (host memory, no GPU use).
+ *
+ * Layouts (total_len is S, cp_size is cp):
+ *  - CPATTN_CONTIGUOUS: the rank's slice [rank*S/cp, (rank+1)*S/cp) — the
+ *    split of the PCP page, §3.5. Needs S % cp == 0.
+ *  - CPATTN_ZIGZAG: the sequence is cut into 2*cp equal chunks and the rank
+ *    takes chunk `rank` and chunk 2*cp-1-rank, so every rank holds early and
+ *    late tokens and the causal work is exactly balanced (zig-zag page, §4.2).
+ *    Needs S % (2*cp) == 0.
+ *  - CPATTN_STRIPED: tokens t with t % cp == rank, the zig-zag page's literal
+ *    example (0, 4, 8, ... on GPU 0 of four). Needs S % cp == 0.
+ *
+ * cu_seqlens == NULL: one sequence. Otherwise cu_seqlens holds n_seqs+1
+ * ascending packed offsets (cu_seqlens[0] == 0, cu_seqlens[n_seqs] == S) and
+ * every document is split on its own with `layout`; the rank's tokens of
+ * document t follow those of document t-1 (each document length must meet the
+ * divisibility rule above).
+ *
+ * out_pos receives S/cp positions in ascending order. out_seq_start
+ * (nullable) receives, per token, the global offset of its document (0
+ * without cu_seqlens).
+ */
+cpattn_status cpattn_zigzag_index(int64_t total_len, int32_t cp_size, int32_t rank, cpattn_layout layout,
+                                  const int32_t *cu_seqlens, int32_t n_seqs,
+                                  int32_t *out_pos, int32_t *out_seq_start);
+
+/*
+ * One arriving KV block folded into a rank's attention state (device memory,
+ * enqueued on `stream`). This is the per-block step of the FCP page, §3.3.
+ *
+ *  q      [lq][hq][head_dim], in_dtype       (bf16 or float32)
+ *  k, v   [lk][hkv][head_dim], in_dtype      (this block's keys and values)
+ *  q_pos  [lq] int32, k_pos [lk] int32       global positions, ascending;
+ *                                            may be NULL only if causal == 0
+ *  causal 1: key j is visible to row i iff k_pos[j] <= q_pos[i]; 0: all keys
+ *  softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ *  o      [lq][hq][head_dim], o_dtype        bf16 input: bf16 or float32 output;
+ *                                            float32 input: float32 output
+ *  lse    [hq][lq] float32
+ *  accumulate 0: write this block's own (O, LSE) (rows with no visible key get
+ *             O = 0, LSE = -inf);
+ *             1: merge this block into the (O, LSE) already in o/lse, in place:
+ *             LSE' = ln(e^LSE + e^LSE_blk), O' = e^(LSE-LSE')·O + e^(LSE_blk-LSE')·O_blk.
+ *             Initialise o = 0, lse = -inf (or make the first call with
+ *             accumulate = 0) before the first block.
+ *
+ * head_dim must be 64 or 128; hq % hkv == 0. Fully masked key tiles are never
+ * loaded. Outputs must not overlap inputs. With lk == 0 (k, v, k_pos may then
+ * be NULL) the block is empty: accumulate = 0 writes O = 0, LSE = -inf and
+ * accumulate = 1 leaves the state unchanged. With lq == 0 nothing is done.
+ */
+cpattn_status cpattn_partial(const void *q, const void *k, const void *v, cpattn_dtype in_dtype,
+                             int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const int32_t *q_pos, const int32_t *k_pos, int32_t causal, float softmax_scale,
+                             void *o, cpattn_dtype o_dtype, float *lse, int32_t accumulate, void *stream);
+
+/*
+ * As cpattn_partial with causal == 1, for packed variable-length documents:
+ * cu_seqlens (DEVICE memory, n_seqs+1 ascending global packed offsets,
+ * cu_seqlens[0] == 0) says where each document starts, and key j is visible to
+ * row i iff seq_start(q_pos[i]) <= k_pos[j] <= q_pos[i], where seq_start(p) is
+ * the largest offset <= p. Every position must be < cu_seqlens[n_seqs].
+ */
+cpattn_status cpattn_varlen_partial(const void *q, const void *k, const void *v, cpattn_dtype in_dtype,
+                                    int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                    const int32_t *q_pos, const int32_t *k_pos,
+                                    const int32_t *cu_seqlens, int32_t n_seqs, float softmax_scale,
+                                    void *o, cpattn_dtype o_dtype, float *lse, int32_t accumulate, void *stream);
+
+/*
+ * In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part)),
+ * the exact combination of two partial results over disjoint key sets (the
+ * global max / global sum normaliser of the PCP page, §4.2, taken two shards
+ * at a time). Commutative, and associative up to rounding, so partials may be
+ * merged in any order (FCP page, §3.3). Device memory, enqueued on `stream`.
+ *
+ *  o_acc, o_part  [lq][hq][head_dim], o_dtype (bf16 or float32)
+ *  lse_acc, lse_part [hq][lq] float32
+ * head_dim must be 64 or 128. o_part/lse_part must not overlap o_acc/lse_acc.
+ */
+cpattn_status cpattn_merge_lse(void *o_acc, float *lse_acc, const void *o_part, const float *lse_part,
+                               cpattn_dtype o_dtype, int64_t lq, int32_t hq, int32_t head_dim, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import context_long_sequence_amd as cp
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cp.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = cp.header_functions()
+    assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
+                          "cpattn_varlen_partial", "cpattn_merge_lse"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert lib.cpattn_version() == 100
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Fake but aligned addresses: every case below is invalid on purpose, so the
+# library must return before touching them. Skipped where a GPU is visible,
+# so that a validation bug could never turn into a launch with these pointers.
+A = 0x10000
+B = 0x20000
+C = 0x30000
+O = 0x40000
+L = 0x50000
+P = 0x60000
+K = 0x70000
+
+# (status name, args for cpattn_partial)
+PARTIAL_CASES = [
+    ("ERR_NULL", (0, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),
+    ("ERR_NULL", (A, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, 0, 0, 0)),
+    ("ERR_NULL", (A, B, C, 0, 8, 8, 1, 1, 64, 0, K, 1, 0.0, O, 0, L, 0, 0)),        # causal needs positions
+    ("ERR_SHAPE", (A, B, C, 0, 8, 8, 1, 1, 96, P, K, 1, 0.0, O, 0, L, 0, 0)),       # head_dim 96
+    ("ERR_SHAPE", (A, B, C, 0, 8, 8, 6, 4, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),       # hq % hkv
+    ("ERR_SHAPE", (A, B, C, 0, -1, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),      # lq < 0
+    ("ERR_SHAPE", (A, B, C, 0, 8, 1 << 31, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),  # lk >= 2^31
+    ("ERR_DTYPE", (A, B, C, 1, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),       # f32 in, bf16 out
+    ("ERR_DTYPE", (A, B, C, 5, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),
+    ("ERR_RANGE", (A, B, C, 0, 8, 8, 1, 1, 64, P, K, 2, 0.0, O, 0, L, 0, 0)),       # causal flag
+    ("ERR_RANGE", (A, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 3, 0)),       # accumulate flag
+    ("ERR_ALIGN", (A + 2, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, L, 0, 0)),
+    ("ERR_ALIGN", (A, B, C, 0, 8, 8, 1, 1, 64, P + 2, K, 1, 0.0, O, 0, L, 0, 0)),
+    ("ERR_ALIAS", (A, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, A + 16, 0, L, 0, 0)),  # o overlaps q
+    ("ERR_ALIAS", (A, B, C, 0, 8, 8, 1, 1, 64, P, K, 1, 0.0, O, 0, B, 0, 0)),       # lse overlaps k
+]
+STATUS = {v: k for k, v in cp.STATUS.items()}
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+@pytest.mark.parametrize("expect,args", PARTIAL_CASES)
+def test_partial_rejects(lib, expect, args):
+    st = lib.cpattn_partial(*args)
+    assert st == STATUS[expect], (st, lib.cpattn_last_error())
+    assert lib.cpattn_last_error().decode()
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+def test_varlen_and_merge_reject(lib):
+    base = (A, B, C, 0, 8, 8, 1, 1, 64, P, K)
+    assert lib.cpattn_varlen_partial(*base, 0, 1, 0.0, O, 0, L, 0, 0) == STATUS["ERR_NULL"]   # no cu_seqlens
+    assert lib.cpattn_varlen_partial(*base, 0x80000, 0, 0.0, O, 0, L, 0, 0) == STATUS["ERR_SHAPE"]  # n_seqs 0
+    assert lib.cpattn_varlen_partial(*base, 0x80002, 1, 0.0, O, 0, L, 0, 0) == STATUS["ERR_ALIGN"]
+    assert lib.cpattn_merge_lse(0, L, C, P, 0, 8, 1, 64, 0) == STATUS["ERR_NULL"]
+    assert lib.cpattn_merge_lse(O, L, C, P, 0, 8, 1, 80, 0) == STATUS["ERR_SHAPE"]
+    assert lib.cpattn_merge_lse(O, L, C, P, 7, 8, 1, 64, 0) == STATUS["ERR_DTYPE"]
+    assert lib.cpattn_merge_lse(O, L, O + 16, P, 0, 8, 1, 64, 0) == STATUS["ERR_ALIAS"]
+    assert lib.cpattn_merge_lse(O + 8, L, C, P, 0, 8, 1, 64, 0) == STATUS["ERR_ALIGN"]
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    out = []
+    pos = np.zeros(4, np.int32)
+    assert lib.cpattn_zigzag_index(16, 4, 9, 1, None, 0, pos.ctypes.data, None) == STATUS["ERR_RANGE"]
+    msg_main = lib.cpattn_last_error().decode()
+
+    def other():
+        out.append(lib.cpattn_last_error().decode())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert msg_main and out == [""]
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(cp.CpattnError):
+        cp.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,361 @@
+"""GPU path (through the C ABI) against the fp64 oracle.
+
+Tolerances: max-abs error <= 2e-2 on bf16 outputs, <= 1e-5 on float32 LSE
+(float32 inputs: <= 1e-4 on O). Each workload runs reduced, where the oracle
+checks every (row, head), and at full size in the same launch configuration
+the benchmark times, where the oracle checks sampled rows and closed forms
+check every row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+O_TOL_BF16 = 2e-2
+O_TOL_F32 = 1e-4
+LSE_TOL = 1e-5
+
+
+def say(msg):
+    print("[gpu-parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle.get()
+
+
+def oracle_share(orc, wl, rows=None, heads=None, blocks=None):
+    """The oracle's result for a workload: positions from its own closed forms,
+    keys of the given blocks (default all) concatenated in block-id order."""
+    docs = wl.doc_lens()
+    qp, qs = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
+    blocks = list(range(wl.n_blocks)) if blocks is None else list(blocks)
+    kps = []
+    for b in blocks:
+        if wl.block_kind == "rank_shares":
+            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
+        elif wl.block_kind == "chunks":
+            c = wl.S // wl.n_blocks
+            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
+        else:
+            kps.append(np.arange(wl.S, dtype=np.int32))
+    k = np.concatenate([wl.kv_block(b, "k") for b in blocks])
+    v = np.concatenate([wl.kv_block(b, "v") for b in blocks])
+    return orc.attention(wl.q(), k, v, qp, np.concatenate(kps), qs if docs is not None else None, True,
+                         rows=rows, heads=heads)
+
+
+def to_np(o, lse):
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def compare(o, lse, o_ref, lse_ref, rows, heads, o_tol, what, lse_tol=LSE_TOL):
+    """o [lq,hq,d] / lse [hq,lq] (numpy) vs oracle rows (rows/heads None = all, row-major)."""
+    lq, hq, d = o.shape
+    if rows is None:
+        og = o.reshape(lq * hq, d)
+        lg = lse.T.reshape(-1)
+    else:
+        og = o[rows, heads]
+        lg = lse[heads, rows]
+    assert np.all(np.isfinite(og)), what + ": non-finite O"
+    assert not np.any(np.isnan(lg)), what + ": NaN LSE"
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lg), empty), what + ": rows with no visible key must have LSE = -inf"
+    eo = float(np.max(np.abs(og - o_ref))) if og.size else 0.0
+    el = float(np.max(np.abs(lg[~empty] - lse_ref[~empty]))) if (~empty).any() else 0.0
+    say("%s: max|dO| = %.3e  max|dLSE| = %.3e  (%d rows)" % (what, eo, el, len(lse_ref)))
+    assert eo <= o_tol, "%s: O error %.3e > %.1e" % (what, eo, o_tol)
+    assert el <= lse_tol, "%s: LSE error %.3e > %.1e" % (what, el, lse_tol)
+    assert np.all(og[empty] == 0.0), what + ": empty rows must have O = 0"
+    return eo, el
+
+
+# ---------------------------------------------------------------------------
+# workloads: reduced (every row) and full size (sampled rows)
+
+def _reduced():
+    from synth import WORKLOADS as W
+    return {
+        "c0": W["c0"],
+        "c1r": W["c1"].scaled(name="c1r", S=4096, hq=4, hkv=4),
+        "c2r": W["c2"].scaled(name="c2r", S=2048),
+        "c3r": W["c3"].scaled(name="c3r", S=8192, hq=4, hkv=4, docs=(256, 2048)),
+        "c4r": W["c4"].scaled(name="c4r", S=16384, hq=8, hkv=2),
+    }
+
+
+@pytest.mark.parametrize("name", ["c0", "c1r", "c2r", "c3r", "c4r"])
+@pytest.mark.parametrize("mode", ["accumulate", "merge"])
+def test_reduced_all_rows(torch_cuda, orc, name, mode):
+    from context_long_sequence_amd.share import share_from_workload
+    wl = _reduced()[name]
+    say("%s mode=%s: S=%d cp=%d hq=%d hkv=%d d=%d %s" % (name, mode, wl.S, wl.cp, wl.hq, wl.hkv, wl.d, wl.dtype))
+    share = share_from_workload(wl)
+    o, lse = share.step(wl.arrival(), mode)
+    torch_cuda.cuda.synchronize()
+    o, lse = to_np(o, lse)
+    o_ref, lse_ref, _ = oracle_share(orc, wl)
+    compare(o, lse, o_ref, lse_ref, None, None, O_TOL_F32 if wl.dtype == "f32" else O_TOL_BF16, name)
+
+
+def test_per_block_partials(torch_cuda, orc):
+    """Each block alone (accumulate = 0), including rows that see nothing in it."""
+    from context_long_sequence_amd.share import share_from_workload
+    for name in ("c0", "c1r", "c4r"):
+        wl = _reduced()[name]
+        share = share_from_workload(wl)
+        for b in range(wl.n_blocks):
+            say("%s block %d alone" % (name, b))
+            share.call_block(b, share.o, share.lse, accumulate=False)
+            torch_cuda.cuda.synchronize()
+            o, lse = to_np(share.o, share.lse)
+            o_ref, lse_ref, _ = oracle_share(orc, wl, blocks=[b])
+            compare(o, lse, o_ref, lse_ref, None, None, O_TOL_F32 if wl.dtype == "f32" else O_TOL_BF16,
+                    "%s block %d" % (name, b))
+
+
+FULL_SAMPLES = {"c1": 512, "c2": 1024, "c3": 512, "c4": 128}
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_size_sampled(torch_cuda, orc, name):
+    from context_long_sequence_amd.share import share_from_workload
+    from synth import WORKLOADS
+    wl = WORKLOADS[name]
+    say("%s full size: generating inputs" % name)
+    share = share_from_workload(wl)
+    say("%s full size: running %d blocks" % (name, wl.n_blocks))
+    o, lse = share.step(wl.arrival(), "accumulate")
+    torch_cuda.cuda.synchronize()
+    o, lse = to_np(o, lse)
+    assert np.all(np.isfinite(o)) and not np.any(np.isnan(lse)) and not np.any(np.isneginf(lse))
+    rows, heads = wl.sample_pairs(FULL_SAMPLES[name])
+    say("%s full size: oracle on %d sampled rows" % (name, len(rows)))
+    o_ref, lse_ref, _ = oracle_share(orc, wl, rows=rows, heads=heads)
+    compare(o, lse, o_ref, lse_ref, rows, heads, O_TOL_BF16, name + " full")
+
+
+def _visible_counts(q_pos, k_pos_all, q_start=None):
+    kp = np.sort(k_pos_all.astype(np.int64))
+    hi = np.searchsorted(kp, q_pos.astype(np.int64), side="right")
+    lo = 0 if q_start is None else np.searchsorted(kp, q_start.astype(np.int64), side="left")
+    return hi - lo, lo, hi
+
+
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_full_size_zero_q_closed_form(torch_cuda, name):
+    """Q = 0 gives uniform weights: LSE = ln(#visible) for EVERY row, and O the
+    mean of the visible values (checked on sampled rows from host prefix sums)."""
+    import torch
+    from context_long_sequence_amd.share import share_from_workload
+    from synth import WORKLOADS, bf16_bits_to_f32
+    wl = WORKLOADS[name]
+    share = share_from_workload(wl)
+    share.q.zero_()
+    o, lse = share.step(wl.arrival(), "accumulate")
+    torch.cuda.synchronize()
+    o, lse = to_np(o, lse)
+    kp_all = np.concatenate(share.k_pos_host)
+    qs = None if share.cu_host is None else np.array(
+        [share.cu_host[np.searchsorted(share.cu_host, p, side="right") - 1] for p in share.q_pos_host], np.int64)
+    cnt, lo, hi = _visible_counts(share.q_pos_host, kp_all, qs)
+    want = np.log(cnt.astype(np.float64))
+    err = float(np.max(np.abs(lse - want[None, :])))
+    say("%s Q=0: max|LSE - ln(count)| = %.3e over %d rows" % (name, err, lse.size))
+    assert err <= LSE_TOL
+    # O on a few rows per head: mean of the visible V rows, in position order
+    order = np.argsort(kp_all, kind="stable")
+    v_all = np.concatenate([wl.kv_block(b, "v") for b in range(wl.n_blocks)])
+    rng = np.random.default_rng(5)
+    rows = rng.choice(wl.lq, size=16, replace=False)
+    for h in range(0, wl.hq, 8):
+        vh = bf16_bits_to_f32(v_all[order, h // (wl.hq // wl.hkv)]).astype(np.float64)
+        pref = np.concatenate([np.zeros((1, wl.d)), np.cumsum(vh, axis=0)])
+        for i in rows:
+            mean = (pref[hi[i]] - pref[lo if np.isscalar(lo) else lo[i]]) / cnt[i]
+            assert np.max(np.abs(o[i, h] - mean)) <= O_TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# properties
+
+
+def test_order_independence_and_determinism(torch_cuda, orc):
+    from context_long_sequence_amd.share import share_from_workload
+    wl = _reduced()["c1r"]
+    share = share_from_workload(wl)
+    outs = []
+    for order in ([0, 1, 2, 3, 4, 5, 6, 7], [7, 6, 5, 4, 3, 2, 1, 0], list(wl.arrival()), [3, 0, 7, 1, 6, 2, 5, 4]):
+        say("c1r order %s" % order)
+        o, lse = share.step(order, "accumulate")
+        torch_cuda.cuda.synchronize()
+        outs.append(to_np(o, lse))
+    o_ref, lse_ref, _ = oracle_share(orc, wl)
+    for o, lse in outs:
+        compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, "c1r any order")
+    for o, lse in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 2 ** -7
+        assert np.max(np.abs(lse - outs[0][1])) <= 4e-6
+    o2, lse2 = to_np(*share.step([0, 1, 2, 3, 4, 5, 6, 7], "accumulate"))
+    assert np.array_equal(o2, outs[0][0]) and np.array_equal(lse2, outs[0][1]), "same order must be bitwise equal"
+
+
+def test_gqa_equals_repeated_kv(torch_cuda):
+    """Grouped KV heads give the same result as KV heads copied per query head."""
+    from context_long_sequence_amd.share import RankShare, share_from_workload
+    wl = _reduced()["c4r"]
+    gqa = share_from_workload(wl)
+    G = wl.hq // wl.hkv
+    rep = RankShare(gqa.q, [k.repeat_interleave(G, dim=1).contiguous() for k in gqa.k_blocks],
+                    [v.repeat_interleave(G, dim=1).contiguous() for v in gqa.v_blocks], gqa.q_pos, gqa.k_pos_blocks)
+    o1, l1 = to_np(*gqa.step(wl.arrival()))
+    o2, l2 = to_np(*rep.step(wl.arrival()))
+    say("GQA vs repeat_kv: max|dO| = %.3e max|dLSE| = %.3e" % (np.max(np.abs(o1 - o2)), np.max(np.abs(l1 - l2))))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_late_block_with_much_larger_scores(torch_cuda, orc):
+    """A late-arriving block whose scores exceed everything before it by a wide
+    margin (its K is scaled by 16) exercises the rescale path. Scores reach
+    ~15 here, so the LSE bound is the workloads' 1e-5 scaled by |LSE| / 10:
+    the float32 rounding of a score grows with its magnitude."""
+    import torch
+    from context_long_sequence_amd.share import share_from_workload
+    from synth import f32_to_bf16_bits, bf16_bits_to_f32
+    wl = _reduced()["c1r"]
+    share = share_from_workload(wl)
+    order = list(wl.arrival())
+    late = order[-1]
+    k_late = f32_to_bf16_bits(bf16_bits_to_f32(wl.kv_block(late, "k")) * np.float32(16.0))
+    share.k_blocks[late] = torch.from_numpy(k_late.view(np.int16)).view(torch.bfloat16).cuda()
+    o, lse = to_np(*share.step(order))
+    # oracle with the same scaled block
+    docs = None
+    qp, _ = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout)
+    kps = [orc.local_positions(wl.S, wl.cp, b, wl.layout)[0] for b in range(wl.n_blocks)]
+    ks = [k_late if b == late else wl.kv_block(b, "k") for b in range(wl.n_blocks)]
+    vs = [wl.kv_block(b, "v") for b in range(wl.n_blocks)]
+    o_ref, lse_ref, _ = orc.attention(wl.q(), np.concatenate(ks), np.concatenate(vs), qp, np.concatenate(kps), docs)
+    top = float(np.max(lse_ref))
+    assert top > 12.0
+    compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, "late large-score block",
+            lse_tol=LSE_TOL * max(1.0, top / 10.0))
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+
+
+def _rand_dev(shape, seed, dtype):
+    import torch
+    from synth import normal_tensor
+    from context_long_sequence_amd.share import bits_to_device
+    return bits_to_device(normal_tensor(shape, seed, "q", 0, 1.0, dtype))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lq,lk,hq,hkv", [(300, 200, 6, 3), (1, 77, 2, 2), (33, 65, 4, 1), (129, 1000, 8, 8)])
+def test_ragged_random_positions(torch_cuda, orc, d, dtype, lq, lk, hq, hkv):
+    """Sizes that are not multiples of any tile, arbitrary ascending positions."""
+    import torch
+    from synth import normal_tensor
+    from context_long_sequence_amd import cpattn_partial
+    from context_long_sequence_amd.share import bits_to_device
+    rng = np.random.default_rng(lq * 7 + lk)
+    qp = np.sort(rng.choice(4 * (lq + lk), size=lq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(4 * (lq + lk), size=lk, replace=False)).astype(np.int32)
+    qh = normal_tensor((lq, hq, d), 11, "q", 0, 1.0, dtype)
+    kh = normal_tensor((lk, hkv, d), 11, "k", 0, 1.0, dtype)
+    vh = normal_tensor((lk, hkv, d), 11, "v", 0, 1.0, dtype)
+    q, k, v = bits_to_device(qh), bits_to_device(kh), bits_to_device(vh)
+    o = torch.empty((lq, hq, d), dtype=q.dtype, device="cuda")
+    lse = torch.empty((hq, lq), dtype=torch.float32, device="cuda")
+    say("ragged lq=%d lk=%d hq=%d hkv=%d d=%d %s" % (lq, lk, hq, hkv, d, dtype))
+    for causal in (True, False):
+        cpattn_partial(q, k, v, torch.from_numpy(qp).cuda(), torch.from_numpy(kp).cuda(), o, lse, causal=causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref, _ = orc.attention(qh, kh, vh, qp, kp, None, causal)
+        compare(*to_np(o, lse), o_ref, lse_ref, None, None, O_TOL_F32 if dtype == "f32" else O_TOL_BF16,
+                "ragged causal=%d" % causal)
+
+
+def test_empty_and_invisible_blocks(torch_cuda):
+    import torch
+    from context_long_sequence_amd import cpattn_partial
+    lq, hq, d = 96, 2, 128
+    q = _rand_dev((lq, hq, d), 1, "bf16")
+    k = _rand_dev((64, hq, d), 2, "bf16")
+    qp = torch.arange(100, 100 + lq, dtype=torch.int32, device="cuda")
+    kp_future = torch.arange(1000, 1064, dtype=torch.int32, device="cuda")   # every key after every query
+    o = torch.empty((lq, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, lq), dtype=torch.float32, device="cuda")
+    say("invisible block, accumulate=0")
+    cpattn_partial(q, k, k, qp, kp_future, o, lse, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+    say("invisible block, accumulate=1 keeps the state")
+    o.copy_(q)
+    lse.fill_(1.25)
+    o0, l0 = o.clone(), lse.clone()
+    cpattn_partial(q, k, k, qp, kp_future, o, lse, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+    say("empty block (lk = 0)")
+    k0 = torch.empty((0, hq, d), dtype=torch.bfloat16, device="cuda")
+    kp0 = torch.empty((0,), dtype=torch.int32, device="cuda")
+    cpattn_partial(q, k0, k0, qp, kp0, o, lse, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+    cpattn_partial(q, k0, k0, qp, kp0, o, lse, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+    say("empty query shard (lq = 0)")
+    q0 = torch.empty((0, hq, d), dtype=torch.bfloat16, device="cuda")
+    cpattn_partial(q0, k, k, torch.empty((0,), dtype=torch.int32, device="cuda"), kp_future,
+                   torch.empty((0, hq, d), dtype=torch.bfloat16, device="cuda"),
+                   torch.empty((hq, 0), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_merge_kernel_against_oracle_merge(torch_cuda, orc):
+    import torch
+    from context_long_sequence_amd import cpattn_merge_lse
+    rng = np.random.default_rng(3)
+    for d, dt in ((64, torch.float32), (128, torch.bfloat16), (128, torch.float32), (64, torch.bfloat16)):
+        lq, hq = 333, 3
+        oa = torch.from_numpy(rng.standard_normal((lq, hq, d)).astype(np.float32)).to(dt).cuda()
+        ob = torch.from_numpy(rng.standard_normal((lq, hq, d)).astype(np.float32)).to(dt).cuda()
+        la = rng.uniform(-5, 15, (hq, lq)).astype(np.float32)
+        lb = rng.uniform(-5, 15, (hq, lq)).astype(np.float32)
+        la[0, :10] = -np.inf
+        lb[0, 5:15] = -np.inf
+        lb[1, 20:30] = la[1, 20:30]
+        ref_o, ref_l = orc.merge(oa.float().cpu().numpy().transpose(1, 0, 2).reshape(-1, d), la.reshape(-1),
+                                 ob.float().cpu().numpy().transpose(1, 0, 2).reshape(-1, d), lb.reshape(-1))
+        lat, lbt = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+        say("merge kernel d=%d %s" % (d, dt))
+        cpattn_merge_lse(oa, lat, ob, lbt)
+        torch.cuda.synchronize()
+        got_o = oa.float().cpu().numpy().transpose(1, 0, 2).reshape(-1, d)
+        got_l = lat.cpu().numpy().reshape(-1)
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isneginf(got_l), ~fin)
+        assert np.max(np.abs(got_l[fin] - ref_l[fin])) <= 4e-6
+        tol = 2 ** -7 * 4 if dt == torch.bfloat16 else 2e-6
+        assert np.max(np.abs(got_o - ref_o)) <= tol
