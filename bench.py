@@ -27,6 +27,38 @@ METRIC = "causal-effective attention TFLOPS per rank share (bf16) + % of MFMA pe
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks (bf16; fp32 matrix)
 
 
+KERNEL_SOURCES = ("partial_fwd.hip", "device_common.hpp", "kernels.hpp")
+
+
+def kernel_source_hash():
+    """sha256 over the partial-attention kernel's sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "context_long_sequence_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary under
+    profiles/, or None when no summary was taken on the current kernel sources
+    for this workload."""
+    import glob
+    import re
+    want = kernel_source_hash()
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+    for path in sorted(glob.glob(os.path.join(root, "*.md"))):
+        text = open(path).read()
+        src = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+        wl = re.search(r"^workload: (\S+)$", text, re.M)
+        tr = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+        if src and wl and tr and src.group(1) == want and wl.group(1) == workload:
+            return int(tr.group(1))
+    return None
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -49,6 +81,9 @@ def main():
     ap.add_argument("--workload", default="c1", help="c0..c4 (default c1, the headline configuration)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain elementwise copy of MIB MiB (read once, written "
+                         "once) a few times: the reference kernel that scales the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -64,6 +99,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     cp.load_library()  # fails loudly if the HIP library is missing
     wl = WORKLOADS[args.workload]
     log("workload %s: %s" % (wl.name, wl.description))
@@ -145,7 +183,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(wl.name),
             "flop_per_launch": kernel_flops,
             "mean_launch_ms": round(kernel_ms, 5),
             "launches": n_launch,
@@ -154,6 +192,21 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, share, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def calibrate_copy(mib, reps=5):
+    """y = -x over MIB MiB of float32: MIB MiB read and MIB MiB written per launch.
+    Profiling this with FETCH_SIZE / WRITE_SIZE gives the counters' scale factor."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4, "launches": reps}),
+          flush=True)
 
 
 def cpu_baseline(wl, share, seconds):
