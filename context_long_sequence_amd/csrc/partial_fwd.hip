@@ -12,29 +12,41 @@
 // GQA support ("长上下文训练 256k 不难", Ulysses section).
 //
 // gfx950 design (not taken from the pages, which give no kernel):
-//  * A workgroup is 4 wave64s. Each wave owns 32 query rows of one head; the
-//    workgroup owns either 128 rows of one head or 32 rows of 4 heads that
-//    share a KV head, so every K/V tile in LDS feeds 128 (row, head) pairs.
+//  * A workgroup is 8 wave64s in two groups of four; wave w runs on SIMD
+//    w % 4, so each SIMD holds one wave of each group. Each wave owns 32 query
+//    rows of one head; the workgroup owns 256 rows of one head, or 32..128
+//    rows of 8..2 heads that share a KV head, so every K/V tile staged in LDS
+//    feeds 256 (row, head) pairs.
+//  * Ping-pong: the two groups alternate, barrier by barrier, between a
+//    matrix phase (P V of tile t, then the scores of tile t+1, on the matrix
+//    cores) and a vector phase (mask, row max, rescale, exp, row sum, bf16
+//    pack of the next tile's scores). While one group's wave on a SIMD issues
+//    MFMAs, the other group's wave on that SIMD does the softmax, so the
+//    softmax costs little beyond the MFMA time. The matrix-phase wave runs at
+//    raised priority (s_setprio) so its MFMAs are not held back.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the accumulator then holds, in each lane, 16
 //    keys of ONE query row (lane % 32), so row max and row sum are in-lane
 //    plus one v_permlane32_swap between the half-waves, and the same
 //    registers, rounded to bf16, are directly the B operand of O^T = V^T P^T.
 //    O^T keeps each lane on one query row too, so the rescale is a per-lane
-//    scalar multiply.
-//  * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4
-//    (no register staging), double-buffered, one barrier per tile. Both are
-//    stored row-major with an XOR swizzle of 16-byte chunks; K is read with
-//    ds_read_b128 (rows = MFMA rows), V with ds_read_b64_tr_b16, which hands
-//    each lane four consecutive keys of one column — the V^T operand layout.
+//    scalar multiply. Q stays in registers for the whole call.
+//  * K and V tiles (64 keys) go global -> LDS with buffer_load_dwordx4 ... lds
+//    (no register staging; lane offsets are loop-invariant, tile and
+//    instruction offsets are scalar) into a ring of three stages, each its
+//    own LDS array, issued a tile and a half ahead and waited for with
+//    counted vmcnt waits. Tiles are row-major with an XOR swizzle of 16-byte
+//    chunks; K is read with ds_read_b128 (rows = MFMA rows), V with
+//    ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
+//    column — the V^T operand layout. The tile's key positions are staged too.
 //  * Softmax runs in base 2 with the scale folded into one FMA per score.
 //    The running max is raised only when a tile's max exceeds it by more than
 //    2^8, so the O rescale is skipped on most tiles (the final normalisation
 //    uses the same stale max, so the result is unchanged).
-//  * Each wave classifies each key tile against its rows from the global
-//    positions: tiles no row can see are skipped, tiles every row sees fully
-//    run without a mask, only boundary tiles are masked. The workgroup loads
-//    only the key range its rows can see.
+//  * The workgroup loads only the key range its rows can see; each wave masks
+//    only tiles it does not see in full (tiles it cannot see at all are
+//    computed and fully masked: within a workgroup's range that is at most a
+//    tile or two per wave near a diagonal or a document start).
 //  * Workgroup ids are remapped so that consecutive logical tiles (same KV
 //    head) run on the same XCD and share its L2; heavy (late-position) query
 //    tiles are scheduled first.
@@ -47,9 +59,9 @@
 
 namespace cpattn {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                 // two groups of four
 constexpr int kThreads = kWaves * 64;
-constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr float kTau = 8.0f;              // lazy-rescale threshold (log2 units)
 
 template <typename TIn, int D>
 struct Cfg {
@@ -57,9 +69,14 @@ struct Cfg {
   static constexpr int kNB = kBf16 ? 2 : 1;           // 32-key blocks per tile
   static constexpr int kBK = 32 * kNB;                // keys per tile
   static constexpr int kRowBytes = D * (int)sizeof(TIn);
-  static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
   static constexpr int kTileBytes = kBK * kRowBytes;
   static constexpr int kInst = kTileBytes / 1024;     // direct-to-LDS instructions per tile
+  static constexpr int kRowsPerInst = 1024 / kRowBytes;
+  static constexpr int kNQ = kBf16 ? D / 16 : D / 2;  // Q operand registers (MFMA k-steps of S^T)
+  static constexpr int kNDT = D / 32;                 // 32-column blocks of O^T
+  static constexpr int kNS = 4;                       // LDS stages of the K/V/position ring
+  // vector-memory instructions one wave issues per load group: K, V, positions
+  static constexpr int kLoadsPerGroup = 2 * (kInst / kWaves) + 1;
   static_assert(kInst % kWaves == 0, "tile must split evenly over the waves");
 
   // Swizzles (16-byte chunk index XOR row function). K is read as 16
@@ -78,6 +95,9 @@ struct Cfg {
   __device__ static __forceinline__ int off_v(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ swz_v(row)) << 4);
   }
+  // the swizzles repeat every 16 rows (K) / 4 rows (bf16 V), a divisor of the
+  // rows one wave's successive load instructions advance by
+  static_assert((kWaves * kRowsPerInst) % 16 == 0, "load offsets must be instruction-invariant");
 };
 
 // Workgroup id -> logical tile id. Hardware dispatches consecutive workgroup
@@ -89,43 +109,141 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + (x < rem ? x : rem) + slot;
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one K or V tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  // raw buffer (stride 0): the record count is a byte count
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Lane part of the source offset of this lane's 16 bytes in a tile's
+// direct-to-LDS instruction inst = wave + kWaves*it: the instruction fills LDS
+// bytes [inst*1024, +1024) with rows inst*RPI .. +RPI-1 of the tile; lane
+// `lane` writes 16 bytes at inst*1024 + 16*lane, which is physical chunk pc
+// of row lr of those, and so must hold logical chunk pc ^ swz(row). The row
+// offset inst*RPI*row_stride is added as a scalar.
 template <typename TIn, int D, bool IS_V>
-__device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char* gbase, int64_t row_stride,
-                                          int64_t j0, int64_t lk, int wave, int lane) {
+__device__ __forceinline__ int lane_voff(int wave, int lane, int64_t row_stride) {
   using C = Cfg<TIn, D>;
+  const int lr = (lane * 16) / C::kRowBytes;
+  const int pc = ((lane * 16) % C::kRowBytes) >> 4;
+  const int row = wave * C::kRowsPerInst + lr;
+  const int chunk = pc ^ (IS_V ? C::swz_v(row) : C::swz_k(row));
+  return lr * (int)row_stride + chunk * 16;
+}
+
+// Issue this wave's share of the direct-to-LDS loads of one K or V tile whose
+// first row is r0. Rows at or past lk re-read the last valid row (they are
+// masked); whole tiles in range need no per-lane arithmetic.
+template <typename TIn, int D, bool IS_V>
+__device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char* head_base, int64_t row_stride,
+                                          int64_t r0, int64_t lk, int wave, int lane, int voff0) {
+  using C = Cfg<TIn, D>;
+  constexpr int RPI = C::kRowsPerInst;
+  const char* base = head_base + r0 * row_stride;
+  const int64_t rows = lk - r0;
+  if (rows >= C::kBK) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (C::kBK - 1) * row_stride + C::kRowBytes);
 #pragma unroll
-  for (int it = 0; it < C::kInst / kWaves; ++it) {
-    int inst = wave + kWaves * it;
-    int o = inst * 1024 + lane * 16;
-    int row = o / C::kRowBytes;
-    int pchunk = (o % C::kRowBytes) >> 4;
-    int chunk = pchunk ^ (IS_V ? C::swz_v(row) : C::swz_k(row));
-    int64_t grow = j0 + row;
-    grow = grow < lk ? grow : lk - 1;  // rows past the block end re-read a valid row; they are masked
-    const char* src = gbase + grow * row_stride + chunk * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (void CPATTN_LDS*)(lds_tile + inst * 1024), 16, 0, 0);
+    for (int it = 0; it < C::kInst / kWaves; ++it) {
+      const int inst = wave + kWaves * it;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void CPATTN_LDS*)(lds_tile + inst * 1024), 16, voff0,
+                                               inst * RPI * (int)row_stride, 0, 0);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (rows - 1) * row_stride + C::kRowBytes);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // the tail tile is rare: recompute its offsets here, keep no registers for them
+    const int lr = (ln * 16) / C::kRowBytes;
+#pragma unroll
+    for (int it = 0; it < C::kInst / kWaves; ++it) {
+      const int inst = wave + kWaves * it;
+      const int row = inst * RPI + lr;
+      const int rc = row < rows ? row : (int)rows - 1;
+      const int voff = lane_voff<TIn, D, IS_V>(wave, ln, row_stride) + (rc - lr) * (int)row_stride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void CPATTN_LDS*)(lds_tile + inst * 1024), 16, voff, 0, 0, 0);
+    }
   }
 }
 
+// Key positions of a tile: wave w loads entries [8w, 8w+8) of the 64-entry
+// stage (the last valid position repeated past lk), one instruction per wave,
+// so every wave issues the same number of loads per group. Without positions
+// (non-causal calls) the same instruction reads the key tensor instead, into
+// a stage nobody reads, to keep that count.
+__device__ __forceinline__ void load_positions(int32_t CPATTN_LDS* kp_tile, const int32_t* src, int64_t r0,
+                                               int64_t lk, int wave, int lane) {
+  const int64_t rows = imin64(lk - r0, 64);
+  const int e = 8 * wave + (lane & 7);
+  const int idx = e < rows ? e : (int)rows - 1;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + r0, rows * 4);
+  if (lane < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void CPATTN_LDS*)(kp_tile + 8 * wave), 4, idx * 4, 0, 0, 0);
+}
+
+// s_waitcnt immediate waiting until at most n vector-memory instructions are outstanding.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier between phases. Unlike __syncthreads() it carries no
+// release fence, which would make every wave wait for ALL of its outstanding
+// direct-to-LDS loads (the prefetch of later stages); the ring waits instead,
+// before the barrier, for exactly the loads it needs. Each wave's LDS reads
+// are complete (lgkmcnt(0)), and the "memory" clobber keeps the compiler from
+// moving memory accesses across.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <typename TIn, typename TOut, int D, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void partial_fwd_kernel(PartialParams p) {
+__global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams p) {
   using C = Cfg<TIn, D>;
   constexpr int NB = C::kNB;
   constexpr int BK = C::kBK;
-  constexpr int NDT = D / 32;
+  constexpr int NDT = C::kNDT;
+  constexpr int NQ = C::kNQ;
+  constexpr int TB = C::kTileBytes;
+  constexpr int NS = C::kNS;
+  constexpr int L = C::kLoadsPerGroup;
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTileBytes];  // [buf][K,V]
-  char CPATTN_LDS* lds = (char CPATTN_LDS*)smem;
+  // LDS ring: a K tile, a V tile and the K tile's key positions per stage.
+  // Every stage is its own array, so the compiler can see that reading one
+  // stage does not alias the direct-to-LDS loads filling another and inserts
+  // no wait for them (the ring's counted waits order them).
+  static_assert(NS == 4, "four LDS stages");
+  __shared__ __attribute__((aligned(1024))) char k_s0[TB], k_s1[TB], k_s2[TB], k_s3[TB];
+  __shared__ __attribute__((aligned(1024))) char v_s0[TB], v_s1[TB], v_s2[TB], v_s3[TB];
+  __shared__ __attribute__((aligned(16))) int32_t p_s0[64], p_s1[64], p_s2[64], p_s3[64];
+  auto kst = [&](auto st) __attribute__((always_inline)) -> char CPATTN_LDS* {
+    constexpr int k = decltype(st)::value;
+    if constexpr (k == 0) return (char CPATTN_LDS*)k_s0;
+    else if constexpr (k == 1) return (char CPATTN_LDS*)k_s1;
+    else if constexpr (k == 2) return (char CPATTN_LDS*)k_s2;
+    else return (char CPATTN_LDS*)k_s3;
+  };
+  auto vst = [&](auto st) __attribute__((always_inline)) -> char CPATTN_LDS* {
+    constexpr int k = decltype(st)::value;
+    if constexpr (k == 0) return (char CPATTN_LDS*)v_s0;
+    else if constexpr (k == 1) return (char CPATTN_LDS*)v_s1;
+    else if constexpr (k == 2) return (char CPATTN_LDS*)v_s2;
+    else return (char CPATTN_LDS*)v_s3;
+  };
+  auto pst = [&](auto st) __attribute__((always_inline)) -> int32_t CPATTN_LDS* {
+    constexpr int k = decltype(st)::value;
+    if constexpr (k == 0) return (int32_t CPATTN_LDS*)p_s0;
+    else if constexpr (k == 1) return (int32_t CPATTN_LDS*)p_s1;
+    else if constexpr (k == 2) return (int32_t CPATTN_LDS*)p_s2;
+    else return (int32_t CPATTN_LDS*)p_s3;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5;        // half-wave
-  const int li = lane & 31;       // query row within the wave
+  const bool grp1 = wave >= kWaves / 2;   // ping-pong group
+  const int g = lane >> 5;                // half-wave
+  const int li = lane & 31;               // query row within the wave
 
-  const int L = xcd_remap(blockIdx.x, p.n_wg);
-  const int hgrp = L / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (L % p.n_qtiles);  // late (heavier) rows first
+  const int Lid = xcd_remap(blockIdx.x, p.n_wg);
+  const int hgrp = Lid / p.n_qtiles;
+  const int qt = p.n_qtiles - 1 - (Lid % p.n_qtiles);  // late (heavier) rows first
   const int hsub = wave % p.g_wg, rb = wave / p.g_wg;
   const int h = hgrp * p.g_wg + hsub;
   const int hk = h / (p.hq / p.hkv);
@@ -137,26 +255,21 @@ __global__ __launch_bounds__(kThreads, 2) void partial_fwd_kernel(PartialParams 
   const int64_t r1 = imin64(r0 + 32, lq);
   const bool wave_active = r0 < lq;
 
-  // ---- key range of the workgroup, and per-wave classification bounds ----
-  int64_t kb = 0, ke = lk;                              // workgroup's visible key range
-  int64_t w_lo = 0, w_hi = lk, f_lo = 0, f_hi = lk;     // wave: visible range, fully visible range
+  // ---- key range of the workgroup, and the per-wave fully visible range ----
+  int64_t kb = 0, ke = lk;                 // workgroup's visible key range
+  int64_t f_lo = 0, f_hi = lk;             // keys every row of this wave sees
   if (p.causal) {
     int32_t wq_hi = p.q_pos[wg_r1 - 1];
     ke = upper_bound_i32(p.k_pos, lk, wq_hi);
     if (VARLEN) kb = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]));
     if (wave_active) {
       int32_t q_lo = p.q_pos[r0], q_hi = p.q_pos[r1 - 1];
-      w_hi = upper_bound_i32(p.k_pos, lk, q_hi);
       f_hi = upper_bound_i32(p.k_pos, lk, q_lo);
-      if (VARLEN) {
-        w_lo = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_lo));
-        f_lo = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_hi));
-      }
+      if (VARLEN) f_lo = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_hi));
     }
   }
-  if (!wave_active) { w_lo = 0; w_hi = 0; }
   const int64_t kt_begin = kb / BK;
-  const int64_t kt_end = (ke + BK - 1) / BK;
+  const int64_t nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads
 
   // ---- this lane's query row ----
   const int64_t qi = imin64(r0 + li, lq - 1);
@@ -165,7 +278,6 @@ __global__ __launch_bounds__(kThreads, 2) void partial_fwd_kernel(PartialParams 
   const int32_t my_start = (VARLEN && p.causal) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
 
   // Q operand (B of S^T = K Q^T), resident in registers for the whole call.
-  constexpr int NQ = C::kBf16 ? D / 16 : D / 2;
   typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
   QReg qreg[NQ];
   {
@@ -187,65 +299,149 @@ __global__ __launch_bounds__(kThreads, 2) void partial_fwd_kernel(PartialParams 
   const char* kbase = (const char*)p.k + (int64_t)hk * D * sizeof(TIn);
   const char* vbase = (const char*)p.v + (int64_t)hk * D * sizeof(TIn);
 
-  if (kt_begin < kt_end) {
-    load_tile<TIn, D, false>(lds, kbase, kv_stride, kt_begin * BK, lk, wave, lane);
-    load_tile<TIn, D, true>(lds + C::kTileBytes, vbase, kv_stride, kt_begin * BK, lk, wave, lane);
+  // ---- loads: group G(t) = {K(t+1) and its positions, V(t)}; tile t lives in stage t % NS ----
+  const int kvoff = lane_voff<TIn, D, false>(wave, lane, kv_stride);
+  const int vvoff = lane_voff<TIn, D, true>(wave, lane, kv_stride);
+  auto load_k = [&](int64_t t, auto st) __attribute__((always_inline)) {
+    const int64_t j0 = (kt_begin + t) * BK;
+    load_tile<TIn, D, false>(kst(st), kbase, kv_stride, j0, lk, wave, lane, kvoff);
+    load_positions(pst(st), p.causal ? p.k_pos : (const int32_t*)p.k, j0, lk, wave, lane);
+  };
+  auto load_v = [&](int64_t t, auto st) __attribute__((always_inline)) {
+    load_tile<TIn, D, true>(vst(st), vbase, kv_stride, (kt_begin + t) * BK, lk, wave, lane, vvoff);
+  };
+
+  // does every row of this wave see every key of tile t?
+  auto tile_full = [&](int64_t t) __attribute__((always_inline)) {
+    const int64_t j0 = (kt_begin + t) * BK;
+    return j0 >= f_lo && j0 + BK <= f_hi;
+  };
+
+  // LDS byte offsets of this lane's MFMA operands (tile-relative, bf16).
+  // K (A of S^T): row li of 32-key block jb, 16-byte chunk 2ks + g.
+  // V^T (A of O^T): transposed 8-byte reads; row 32jb + 16h + vr (+8), column block dt.
+  int kaddr[C::kBf16 ? NQ : 1];
+  int vaddr[C::kBf16 ? NDT : 1];
+  if constexpr (C::kBf16) {
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) kaddr[ks] = C::off_k(li, 2 * ks + g);
+    const int vr = 4 * g + ((lane & 15) >> 2);              // row within a 16-key group
+    const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-column block
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int col = 32 * dt + vc;
+      vaddr[dt] = C::off_v(vr, col >> 3) + ((col & 7) << 1);
+    }
   }
 
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
-    const int cur = (int)((kt - kt_begin) & 1);
-    char CPATTN_LDS* kl = lds + cur * 2 * C::kTileBytes;
-    char CPATTN_LDS* vl = kl + C::kTileBytes;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt are in LDS
-    __syncthreads();                     // everyone's are; and tile kt-1's buffer is free
-    if (kt + 1 < kt_end) {
-      char CPATTN_LDS* nk = lds + (cur ^ 1) * 2 * C::kTileBytes;
-      load_tile<TIn, D, false>(nk, kbase, kv_stride, (kt + 1) * BK, lk, wave, lane);
-      load_tile<TIn, D, true>(nk + C::kTileBytes, vbase, kv_stride, (kt + 1) * BK, lk, wave, lane);
-    }
+  f32x16_t sacc[NB];        // scores of the tile in flight (S^T, one query row per lane)
+  uint32_t pk[NB][8];       // its probabilities packed to bf16 pairs (bf16 path)
 
-    const int64_t j0 = kt * BK, j1 = j0 + BK;
-    if (j1 <= w_lo || j0 >= w_hi) continue;             // no row of this wave sees the tile
-    const bool full = (j0 >= f_lo) && (j1 <= f_hi);     // every row sees every key
-
-    // ---- S^T = K Q^T for NB blocks of 32 keys ----
-    f32x16_t sacc[NB];
+  // ---- matrix phase pieces ----
+  // The operand reads are software-pipelined by hand, RING operands ahead of
+  // the MFMA that consumes them, and fenced with sched_barrier so that the
+  // compiler keeps that order (left alone it reads each operand right before
+  // its MFMA and waits out the LDS latency every time).
+  constexpr int RING = 4;
+  // S^T = K Q^T for one tile: NQ*NB MFMAs.
+  auto qk_tile = [&](const char CPATTN_LDS* kl) __attribute__((always_inline)) {
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb) {
-      sacc[jb] = f32x16_t{};
-      const int row = 32 * jb + li;
+    for (int jb = 0; jb < NB; ++jb) sacc[jb] = f32x16_t{};
+    if constexpr (C::kBf16) {
+      constexpr int NM = NQ * NB;
+      auto rd = [&](int s) __attribute__((always_inline)) {
+        return *(const bf16x8_t CPATTN_LDS*)(kl + kaddr[s / NB] + (s % NB) * 32 * C::kRowBytes);
+      };
+      bf16x8_t ka[RING];
+#pragma unroll
+      for (int s = 0; s < RING; ++s) ka[s] = rd(s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < NM; ++s) {
+        sacc[s % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % RING], qreg[s / NB], sacc[s % NB], 0, 0, 0);
+        if (s + RING < NM) ka[s % RING] = rd(s + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
       for (int ks = 0; ks < NQ; ++ks) {
-        if constexpr (C::kBf16) {
-          bf16x8_t a = *(const bf16x8_t CPATTN_LDS*)(kl + C::off_k(row, 2 * ks + g));
-          sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[jb], 0, 0, 0);
-        } else {
-          const int d = 2 * ks + g;
-          float a = *(const float CPATTN_LDS*)(kl + C::off_k(row, d >> 2) + ((d & 3) << 2));
-          sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qreg[ks], sacc[jb], 0, 0, 0);
+        const int d = 2 * ks + g;
+        float a = *(const float CPATTN_LDS*)(kl + C::off_k(li, d >> 2) + ((d & 3) << 2));
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qreg[ks], sacc[0], 0, 0, 0);
+      }
+    }
+  };
+
+  // O^T += V^T P^T for one tile.
+  auto pv_tile = [&](const char CPATTN_LDS* vl) __attribute__((always_inline)) {
+    if constexpr (C::kBf16) {
+      constexpr int NM = 2 * NB * NDT;
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      // V^T operand of MFMA m = (jb, hf, dt): keys 32jb + 16hf + vr (and + 8), column block dt
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        const int jb = m / (2 * NDT), hf = (m / NDT) % 2, dt = m % NDT;
+        const int roff = (32 * jb + 16 * hf) * C::kRowBytes;
+        i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t CPATTN_LDS*)(vl + vaddr[dt] + roff));
+        i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t CPATTN_LDS*)(vl + vaddr[dt] + roff + 8 * C::kRowBytes));
+        return __builtin_bit_cast(bf16x8_t, (i16x8)__builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t va[RING];
+#pragma unroll
+      for (int m = 0; m < RING; ++m) va[m] = rd(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int jb = m / (2 * NDT), hf = (m / NDT) % 2, dt = m % NDT;
+        const u32x4 bw = {pk[jb][4 * hf], pk[jb][4 * hf + 1], pk[jb][4 * hf + 2], pk[jb][4 * hf + 3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % RING], __builtin_bit_cast(bf16x8_t, bw), oacc[dt],
+                                                           0, 0, 0);
+        if (m + RING < NM) va[m % RING] = rd(m + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // float32: P stays in the score registers (already exponentiated)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const int row = 8 * (ks >> 2) + 4 * g + (ks & 3);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int col = 32 * dt + li;
+          float a = *(const float CPATTN_LDS*)(vl + C::off_v(row, col >> 2) + ((col & 3) << 2));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[0][ks], oacc[dt], 0, 0, 0);
         }
       }
     }
+  };
 
-    // ---- mask boundary tiles: lane's register r of block jb is key 32jb + 8(r/4) + 4g + r%4 ----
-    if (!full) {
+  // ---- vector phase: mask, max, rescale, exp, sum, pack of tile t's scores ----
+  // Boundary tiles: lane register r of block jb is key 32jb + 8(r/4) + 4g + r%4
+  // of the tile. Keys at or past lk and keys the lane's row cannot see get -inf.
+  auto mask = [&](const int32_t CPATTN_LDS* kp, int64_t t) __attribute__((always_inline)) {
+    const int lim = (int)imin64(lk - (kt_begin + t) * BK, BK);  // keys of the tile inside the block
+    const int go = 4 * g;
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
+    for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-          bool vis = j < lk;
-          if (vis && p.causal) {
-            const int32_t kp = p.k_pos[j];
-            vis = kp <= my_qpos;
-            if (VARLEN) vis = vis && kp >= my_start;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int jt = 32 * jb + 8 * rr;
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+        i32x4 kv = {0, 0, 0, 0};
+        if (p.causal) kv = *(const i32x4 CPATTN_LDS*)(kp + go + jt);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bool vis = go + jt + c < lim;
+          if (p.causal) {
+            vis = vis & (kv[c] <= my_qpos);
+            if (VARLEN) vis = vis & (kv[c] >= my_start);
           }
-          if (!vis) sacc[jb][r] = neg_inf();
+          sacc[jb][4 * rr + c] = vis ? sacc[jb][4 * rr + c] : neg_inf();
         }
       }
-    }
-
-    // ---- online softmax (base 2) ----
+  };
+  auto softmax_tile = [&](const int32_t CPATTN_LDS* kp, int64_t t) __attribute__((always_inline)) {
+    if (!tile_full(t)) mask(kp, t);
     float mx = neg_inf();
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
@@ -264,59 +460,72 @@ __global__ __launch_bounds__(kThreads, 2) void partial_fwd_kernel(PartialParams 
       m_run = m_new;
     }
     const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-    float lsum = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], p.scale_log2, -m_use));
-        sacc[jb][r] = e;
-        lsum += e;
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], p.scale_log2, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r + 1], p.scale_log2, -m_use));
+        ls0 += e0;
+        ls1 += e1;
+        if constexpr (C::kBf16) {
+          pk[jb][r / 2] = pack_bf16x2(e0, e1);
+        } else {
+          sacc[jb][r] = e0;
+          sacc[jb][r + 1] = e1;
+        }
       }
-    l_run += lsum;
+    l_run += ls0 + ls1;
+  };
 
-    // ---- O^T += V^T P^T ----
-    if constexpr (C::kBf16) {
-      uint32_t pk[NB][8];
-#pragma unroll
-      for (int jb = 0; jb < NB; ++jb)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) pk[jb][r] = pack_bf16x2(sacc[jb][2 * r], sacc[jb][2 * r + 1]);
-      const int vr = 4 * g + ((lane & 15) >> 2);             // row within a 16-key group
-      const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-column block
-#pragma unroll
-      for (int jb = 0; jb < NB; ++jb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          u32x4 bw = {pk[jb][4 * half], pk[jb][4 * half + 1], pk[jb][4 * half + 2], pk[jb][4 * half + 3]};
-          bf16x8_t b = __builtin_bit_cast(bf16x8_t, bw);
-          const int row = 32 * jb + 16 * half + vr;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int col = 32 * dt + vc;
-            const int cb = (col & 7) << 1;
-            i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4_t CPATTN_LDS*)(vl + C::off_v(row, col >> 3) + cb));
-            i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4_t CPATTN_LDS*)(vl + C::off_v(row + 8, col >> 3) + cb));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            i16x8 a16 = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a16), b, oacc[dt], 0, 0, 0);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const int row = 8 * (ks >> 2) + 4 * g + (ks & 3);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int col = 32 * dt + li;
-          float a = *(const float CPATTN_LDS*)(vl + C::off_v(row, col >> 2) + ((col & 3) << 2));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[0][ks], oacc[dt], 0, 0, 0);
-        }
-      }
+  // ---- ping-pong schedule ----
+  // Every wave runs the same program: for each tile t, the vector step of t,
+  // a barrier, the matrix step of t (P V of t, scores of t+1), a barrier.
+  // Group 1 starts one barrier later than group 0 (and group 0 ends with one
+  // more), so at every phase one group is in its matrix step and the other
+  // in its vector step. Tile j's K, positions and V live in stage j % NS.
+  // Iteration t first issues load group G(t+2) = {K(t+3), its positions,
+  // V(t+2)} into the stages of K(t-1) and V(t-2), which every wave has
+  // finished with by then (in either group's phase offset), and ends by
+  // waiting for G(t+1) = {K(t+2), positions, V(t+1)}, which the next matrix
+  // step needs, with G(t+2) left in flight.
+  auto iteration = [&](int64_t t, auto sk) __attribute__((always_inline)) {
+    constexpr int k = decltype(sk)::value;
+    const std::integral_constant<int, (k + 1) % NS> sn{};
+    const std::integral_constant<int, (k + 2) % NS> s2{};
+    const std::integral_constant<int, (k + 3) % NS> s3{};
+    if (t + 3 < nt) load_k(t + 3, s3);
+    if (t + 2 < nt) load_v(t + 2, s2);
+    softmax_tile(pst(sk), t);
+    phase_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    pv_tile(vst(sk));
+    if (t + 1 < nt) qk_tile(kst(sn));
+    __builtin_amdgcn_s_setprio(0);
+    if (t + 3 < nt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    phase_barrier();
+  };
+
+  if (nt > 0) {
+    // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)}
+    load_k(0, S0{});
+    if (1 < nt) load_k(1, S1{});
+    load_v(0, S0{});
+    if (2 < nt) load_k(2, S2{});
+    if (1 < nt) load_v(1, S1{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    phase_barrier();
+    qk_tile(kst(S0{}));
+    if (grp1) phase_barrier();
+    for (int64_t t = 0; t < nt; t += NS) {
+      iteration(t, S0{});
+      if (t + 1 < nt) iteration(t + 1, S1{});
+      if (t + 2 < nt) iteration(t + 2, S2{});
+      if (t + 3 < nt) iteration(t + 3, S3{});
     }
+    if (!grp1) phase_barrier();
   }
 
   // ---- finalise: O = acc / l, LSE = ln(l) + max; merge into the stored state if accumulating ----
@@ -371,8 +580,9 @@ static hipError_t launch_typed(const PartialParams& p, bool varlen, hipStream_t 
 }
 
 hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_dim, bool varlen, hipStream_t stream) {
+  // a workgroup: g_wg query heads of one KV group x r_wg blocks of 32 rows, g_wg * r_wg = kWaves
   const int G = p.hq / p.hkv;
-  p.g_wg = (G % kWaves == 0) ? kWaves : ((G % 2 == 0) ? 2 : 1);
+  p.g_wg = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   p.r_wg = kWaves / p.g_wg;
   p.n_qtiles = (int32_t)((p.lq + 32 * p.r_wg - 1) / (32 * p.r_wg));
   p.n_hgroups = p.hq / p.g_wg;
