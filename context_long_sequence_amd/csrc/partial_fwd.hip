@@ -190,6 +190,15 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // moving memory accesses across.
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Materialise a register value at this point of the program. The barrier above
+// only orders memory accesses: left alone, the compiler sinks pure register
+// work (the exponentials, packs and row sums of the vector phase) past it into
+// the wave's own matrix phase, which serialises the two phases the schedule
+// means to overlap across waves. An empty volatile asm that reads and writes
+// the value keeps its computation before the next volatile asm (the barrier).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+
 template <typename TIn, typename TOut, int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams p) {
   using C = Cfg<TIn, D>;
@@ -338,11 +347,12 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   uint32_t pk[NB][8];       // its probabilities packed to bf16 pairs (bf16 path)
 
   // ---- matrix phase pieces ----
-  // The operand reads are software-pipelined by hand, RING operands ahead of
+  // The operand reads are software-pipelined by hand, RING_* operands ahead of
   // the MFMA that consumes them, and fenced with sched_barrier so that the
   // compiler keeps that order (left alone it reads each operand right before
   // its MFMA and waits out the LDS latency every time).
-  constexpr int RING = 4;
+  constexpr int RING_K = 4;   // K operands in flight
+  constexpr int RING_V = 4;   // V^T operands in flight
   // S^T = K Q^T for one tile: NQ*NB MFMAs.
   auto qk_tile = [&](const char CPATTN_LDS* kl) __attribute__((always_inline)) {
 #pragma unroll
@@ -352,14 +362,14 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       auto rd = [&](int s) __attribute__((always_inline)) {
         return *(const bf16x8_t CPATTN_LDS*)(kl + kaddr[s / NB] + (s % NB) * 32 * C::kRowBytes);
       };
-      bf16x8_t ka[RING];
+      bf16x8_t ka[RING_K];
 #pragma unroll
-      for (int s = 0; s < RING; ++s) ka[s] = rd(s);
+      for (int s = 0; s < RING_K; ++s) ka[s] = rd(s);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < NM; ++s) {
-        sacc[s % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % RING], qreg[s / NB], sacc[s % NB], 0, 0, 0);
-        if (s + RING < NM) ka[s % RING] = rd(s + RING);
+        sacc[s % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % RING_K], qreg[s / NB], sacc[s % NB], 0, 0, 0);
+        if (s + RING_K < NM) ka[s % RING_K] = rd(s + RING_K);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -387,17 +397,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
             (i16x4_t CPATTN_LDS*)(vl + vaddr[dt] + roff + 8 * C::kRowBytes));
         return __builtin_bit_cast(bf16x8_t, (i16x8)__builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8_t va[RING];
+      bf16x8_t va[RING_V];
 #pragma unroll
-      for (int m = 0; m < RING; ++m) va[m] = rd(m);
+      for (int m = 0; m < RING_V; ++m) va[m] = rd(m);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int jb = m / (2 * NDT), hf = (m / NDT) % 2, dt = m % NDT;
         const u32x4 bw = {pk[jb][4 * hf], pk[jb][4 * hf + 1], pk[jb][4 * hf + 2], pk[jb][4 * hf + 3]};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % RING], __builtin_bit_cast(bf16x8_t, bw), oacc[dt],
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m % RING_V], __builtin_bit_cast(bf16x8_t, bw), oacc[dt],
                                                            0, 0, 0);
-        if (m + RING < NM) va[m % RING] = rd(m + RING);
+        if (m + RING_V < NM) va[m % RING_V] = rd(m + RING_V);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -477,6 +487,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         }
       }
     l_run += ls0 + ls1;
+    // the vector phase's results exist before the barrier that follows it
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      if constexpr (C::kBf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pin(pk[jb][i]);
+      } else {
+        pin(sacc[jb]);
+      }
+    }
+    pin(l_run);
   };
 
   // ---- ping-pong schedule ----
