@@ -84,6 +84,9 @@ cpattn_status check_partial_args(const void* q, const void* k, const void* v, cp
   if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
   if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
   if ((int64_t)hq * head_dim * lq >= (int64_t)1 << 40) return fail(CPATTN_ERR_SHAPE, "q is too large");
+  // the kernel addresses a 64-key tile of one KV head with 32-bit buffer offsets
+  if ((int64_t)hkv * head_dim * (int64_t)dsize(in_dtype) * 64 >= (int64_t)1 << 31)
+    return fail(CPATTN_ERR_SHAPE, "hkv * head_dim too large (a 64-key KV tile must span < 2 GiB)");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(CPATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
   if (!aligned(lse, 4) || (q_pos && !aligned(q_pos, 4)) || (k_pos && !aligned(k_pos, 4)))

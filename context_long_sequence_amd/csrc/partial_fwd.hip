@@ -75,8 +75,6 @@ struct Cfg {
   static constexpr int kNQ = kBf16 ? D / 16 : D / 2;  // Q operand registers (MFMA k-steps of S^T)
   static constexpr int kNDT = D / 32;                 // 32-column blocks of O^T
   static constexpr int kNS = 4;                       // LDS stages of the K/V/position ring
-  // vector-memory instructions one wave issues per load group: K, V, positions
-  static constexpr int kLoadsPerGroup = 2 * (kInst / kWaves) + 1;
   static_assert(kInst % kWaves == 0, "tile must split evenly over the waves");
 
   // Swizzles (16-byte chunk index XOR row function). K is read as 16
@@ -135,11 +133,11 @@ __device__ __forceinline__ int lane_voff(int wave, int lane, int64_t row_stride)
 // masked); whole tiles in range need no per-lane arithmetic.
 template <typename TIn, int D, bool IS_V>
 __device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char* head_base, int64_t row_stride,
-                                          int64_t r0, int64_t lk, int wave, int lane, int voff0) {
+                                          int r0, int lk, int wave, int lane, int voff0) {
   using C = Cfg<TIn, D>;
   constexpr int RPI = C::kRowsPerInst;
-  const char* base = head_base + r0 * row_stride;
-  const int64_t rows = lk - r0;
+  const char* base = head_base + (int64_t)r0 * row_stride;
+  const int rows = lk - r0;
   if (rows >= C::kBK) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (C::kBK - 1) * row_stride + C::kRowBytes);
 #pragma unroll
@@ -157,7 +155,7 @@ __device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char*
     for (int it = 0; it < C::kInst / kWaves; ++it) {
       const int inst = wave + kWaves * it;
       const int row = inst * RPI + lr;
-      const int rc = row < rows ? row : (int)rows - 1;
+      const int rc = row < rows ? row : rows - 1;
       const int voff = lane_voff<TIn, D, IS_V>(wave, ln, row_stride) + (rc - lr) * (int)row_stride;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void CPATTN_LDS*)(lds_tile + inst * 1024), 16, voff, 0, 0, 0);
     }
@@ -169,14 +167,72 @@ __device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char*
 // so every wave issues the same number of loads per group. Without positions
 // (non-causal calls) the same instruction reads the key tensor instead, into
 // a stage nobody reads, to keep that count.
-__device__ __forceinline__ void load_positions(int32_t CPATTN_LDS* kp_tile, const int32_t* src, int64_t r0,
-                                               int64_t lk, int wave, int lane) {
-  const int64_t rows = imin64(lk - r0, 64);
+__device__ __forceinline__ void load_positions(int32_t CPATTN_LDS* kp_tile, const int32_t* src, int r0, int lk,
+                                               int wave, int lane) {
+  const int rows = min(lk - r0, 64);
   const int e = 8 * wave + (lane & 7);
-  const int idx = e < rows ? e : (int)rows - 1;
+  const int idx = e < rows ? e : rows - 1;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + r0, rows * 4);
   if (lane < 8)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void CPATTN_LDS*)(kp_tile + 8 * wave), 4, idx * 4, 0, 0, 0);
+}
+
+// Register-staged loads for the steady-state ring. Direct-to-LDS loads have a
+// small in-flight budget per CU: once about sixteen are outstanding, issuing
+// one more stalls the wave until an earlier one lands (hundreds of cycles when
+// the data streams from HBM). Loads into registers issue in a few cycles
+// however many are in flight, so the ring fetches the next load group into
+// registers one phase pair ahead and writes it to LDS (ds_write_b128) when it
+// is needed. The lane/instruction mapping is that of load_tile, so the LDS
+// layout is the same.
+//
+// The fetch has no branches: the buffer descriptor covers exactly the tile's
+// rows inside the block, and the hardware range check returns zeros for the
+// lanes of rows past it (a tail tile's missing keys, or a whole tile past the
+// end, which is then never read). Zero rows are harmless: their scores are
+// masked and their probabilities are zero. The row offset goes into the
+// per-lane offset, which the range check sees.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// n (wave-uniform) clamped to [0, hi]. The clamp is selected as a vector
+// instruction (v_med3); reading the result back as a scalar keeps the buffer
+// descriptor built from it in scalar registers (a descriptor the compiler
+// thinks may vary per lane costs a loop over lanes at every load).
+__device__ __forceinline__ int clamp_rows(int n, int hi) {
+  n = n < hi ? n : hi;
+  return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
+}
+
+template <typename TIn, int D>
+__device__ __forceinline__ void fetch_tile(u32x4_t* regs, const char* head_base, int row_stride, int r0, int lk,
+                                           int wave, int voff0) {
+  using C = Cfg<TIn, D>;
+  constexpr int RPI = C::kRowsPerInst;
+  const int rows = clamp_rows(lk - r0, C::kBK);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head_base + (int64_t)r0 * row_stride, (int64_t)rows * row_stride);
+#pragma unroll
+  for (int it = 0; it < C::kInst / kWaves; ++it)
+    regs[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0 + (wave + kWaves * it) * RPI * row_stride, 0, 0);
+}
+
+template <typename TIn, int D>
+__device__ __forceinline__ void commit_tile(char CPATTN_LDS* lds_tile, const u32x4_t* regs, int wave, int lane) {
+  using C = Cfg<TIn, D>;
+#pragma unroll
+  for (int it = 0; it < C::kInst / kWaves; ++it)
+    *(u32x4_t CPATTN_LDS*)(lds_tile + (wave + kWaves * it) * 1024 + lane * 16) = regs[it];
+}
+
+// Positions: lanes 0..7 of wave w hold entries 8w..8w+7 (zero past the block,
+// and everywhere when src is null: non-causal calls stage zeros nobody reads).
+__device__ __forceinline__ int32_t fetch_positions(const int32_t* src, int r0, int lk, int wave, int lane) {
+  const int rows = src ? clamp_rows(lk - r0, 64) : 0;
+  return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(src + r0, rows * 4), (8 * wave + (lane & 7)) * 4,
+                                                       0, 0);
+}
+
+__device__ __forceinline__ void commit_positions(int32_t CPATTN_LDS* kp_tile, int32_t v, int wave, int lane) {
+  if (lane < 8) kp_tile[8 * wave + lane] = v;
 }
 
 // s_waitcnt immediate waiting until at most n vector-memory instructions are outstanding.
@@ -208,7 +264,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   constexpr int NQ = C::kNQ;
   constexpr int TB = C::kTileBytes;
   constexpr int NS = C::kNS;
-  constexpr int L = C::kLoadsPerGroup;
 
   // LDS ring: a K tile, a V tile and the K tile's key positions per stage.
   // Every stage is its own array, so the compiler can see that reading one
@@ -257,31 +312,33 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int h = hgrp * p.g_wg + hsub;
   const int hk = h / (p.hq / p.hkv);
 
-  const int64_t lq = p.lq, lk = p.lk;
-  const int64_t wg_r0 = (int64_t)qt * 32 * p.r_wg;
-  const int64_t wg_r1 = imin64(wg_r0 + 32 * p.r_wg, lq);
-  const int64_t r0 = wg_r0 + 32 * rb;
-  const int64_t r1 = imin64(r0 + 32, lq);
+  // row and key indices fit in 32 bits (the host checks lq, lk < 2^31), which
+  // keeps the tile bookkeeping on the scalar unit
+  const int lq = (int)p.lq, lk = (int)p.lk;
+  const int wg_r0 = qt * 32 * p.r_wg;
+  const int wg_r1 = min(wg_r0 + 32 * p.r_wg, lq);
+  const int r0 = wg_r0 + 32 * rb;
+  const int r1 = min(r0 + 32, lq);
   const bool wave_active = r0 < lq;
 
   // ---- key range of the workgroup, and the per-wave fully visible range ----
-  int64_t kb = 0, ke = lk;                 // workgroup's visible key range
-  int64_t f_lo = 0, f_hi = lk;             // keys every row of this wave sees
+  int kb = 0, ke = lk;                     // workgroup's visible key range
+  int f_lo = 0, f_hi = lk;                 // keys every row of this wave sees
   if (p.causal) {
     int32_t wq_hi = p.q_pos[wg_r1 - 1];
-    ke = upper_bound_i32(p.k_pos, lk, wq_hi);
-    if (VARLEN) kb = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]));
+    ke = (int)upper_bound_i32(p.k_pos, lk, wq_hi);
+    if (VARLEN) kb = (int)lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]));
     if (wave_active) {
       int32_t q_lo = p.q_pos[r0], q_hi = p.q_pos[r1 - 1];
-      f_hi = upper_bound_i32(p.k_pos, lk, q_lo);
-      if (VARLEN) f_lo = lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_hi));
+      f_hi = (int)upper_bound_i32(p.k_pos, lk, q_lo);
+      if (VARLEN) f_lo = (int)lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_hi));
     }
   }
-  const int64_t kt_begin = kb / BK;
-  const int64_t nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads
+  const int kt_begin = kb / BK;
+  const int nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads
 
   // ---- this lane's query row ----
-  const int64_t qi = imin64(r0 + li, lq - 1);
+  const int qi = min(r0 + li, lq - 1);
   const bool row_valid = wave_active && (r0 + li < lq);
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
   const int32_t my_start = (VARLEN && p.causal) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
@@ -290,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
   QReg qreg[NQ];
   {
-    const TIn* qrow = (const TIn*)p.q + (qi * p.hq + h) * (int64_t)D;
+    const TIn* qrow = (const TIn*)p.q + ((int64_t)qi * p.hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       if constexpr (C::kBf16) qreg[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * g);
@@ -311,18 +368,33 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // ---- loads: group G(t) = {K(t+1) and its positions, V(t)}; tile t lives in stage t % NS ----
   const int kvoff = lane_voff<TIn, D, false>(wave, lane, kv_stride);
   const int vvoff = lane_voff<TIn, D, true>(wave, lane, kv_stride);
-  auto load_k = [&](int64_t t, auto st) __attribute__((always_inline)) {
-    const int64_t j0 = (kt_begin + t) * BK;
+  auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
+    const int j0 = (kt_begin + t) * BK;
     load_tile<TIn, D, false>(kst(st), kbase, kv_stride, j0, lk, wave, lane, kvoff);
     load_positions(pst(st), p.causal ? p.k_pos : (const int32_t*)p.k, j0, lk, wave, lane);
   };
-  auto load_v = [&](int64_t t, auto st) __attribute__((always_inline)) {
+  auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
     load_tile<TIn, D, true>(vst(st), vbase, kv_stride, (kt_begin + t) * BK, lk, wave, lane, vvoff);
+  };
+  // steady state: G(j) is fetched into registers one period ahead, then committed to its stages
+  u32x4_t kreg[C::kInst / kWaves], vreg[C::kInst / kWaves];
+  int32_t preg = 0;
+  // (for j = nt-1 the K part reads nothing and writes zeros to a free stage)
+  auto fetch_group = [&](int j) __attribute__((always_inline)) {  // requires j < nt
+    const int j0 = (kt_begin + j) * BK;
+    fetch_tile<TIn, D>(kreg, kbase, (int)kv_stride, j0 + BK, lk, wave, kvoff);
+    preg = fetch_positions(p.causal ? p.k_pos : nullptr, j0 + BK, lk, wave, lane);
+    fetch_tile<TIn, D>(vreg, vbase, (int)kv_stride, j0, lk, wave, vvoff);
+  };
+  auto commit_group = [&](auto sk1, auto sv) __attribute__((always_inline)) {
+    commit_tile<TIn, D>(kst(sk1), kreg, wave, lane);
+    commit_positions(pst(sk1), preg, wave, lane);
+    commit_tile<TIn, D>(vst(sv), vreg, wave, lane);
   };
 
   // does every row of this wave see every key of tile t?
-  auto tile_full = [&](int64_t t) __attribute__((always_inline)) {
-    const int64_t j0 = (kt_begin + t) * BK;
+  auto tile_full = [&](int t) __attribute__((always_inline)) {
+    const int j0 = (kt_begin + t) * BK;
     return j0 >= f_lo && j0 + BK <= f_hi;
   };
 
@@ -428,8 +500,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // ---- vector phase: mask, max, rescale, exp, sum, pack of tile t's scores ----
   // Boundary tiles: lane register r of block jb is key 32jb + 8(r/4) + 4g + r%4
   // of the tile. Keys at or past lk and keys the lane's row cannot see get -inf.
-  auto mask = [&](const int32_t CPATTN_LDS* kp, int64_t t) __attribute__((always_inline)) {
-    const int lim = (int)imin64(lk - (kt_begin + t) * BK, BK);  // keys of the tile inside the block
+  auto mask = [&](const int32_t CPATTN_LDS* kp, int t) __attribute__((always_inline)) {
+    const int lim = min(lk - (kt_begin + t) * BK, BK);  // keys of the tile inside the block
     const int go = 4 * g;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
@@ -450,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         }
       }
   };
-  auto softmax_tile = [&](const int32_t CPATTN_LDS* kp, int64_t t) __attribute__((always_inline)) {
+  auto softmax_tile = [&](const int32_t CPATTN_LDS* kp, int t) __attribute__((always_inline)) {
     if (!tile_full(t)) mask(kp, t);
     float mx = neg_inf();
 #pragma unroll
@@ -506,31 +578,37 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // Group 1 starts one barrier later than group 0 (and group 0 ends with one
   // more), so at every phase one group is in its matrix step and the other
   // in its vector step. Tile j's K, positions and V live in stage j % NS.
-  // Iteration t first issues load group G(t+2) = {K(t+3), its positions,
-  // V(t+2)} into the stages of K(t-1) and V(t-2), which every wave has
-  // finished with by then (in either group's phase offset), and ends by
-  // waiting for G(t+1) = {K(t+2), positions, V(t+1)}, which the next matrix
-  // step needs, with G(t+2) left in flight.
-  auto iteration = [&](int64_t t, auto sk) __attribute__((always_inline)) {
+  // Load group G(j) = {K(j+1), its positions, V(j)}. Iteration t fetches
+  // G(t+2) into registers as it starts, and its matrix step ends by
+  // committing them to the stages of K(t-1) and V(t-2), which every wave has
+  // finished with by then in either group's phase offset. The barrier that
+  // follows publishes the commit; its first readers (the matrix step of t+2,
+  // the vector step of t+3) are at least one more barrier away for both
+  // groups.
+  auto iteration = [&](int t, auto sk) __attribute__((always_inline)) {
     constexpr int k = decltype(sk)::value;
     const std::integral_constant<int, (k + 1) % NS> sn{};
     const std::integral_constant<int, (k + 2) % NS> s2{};
     const std::integral_constant<int, (k + 3) % NS> s3{};
-    if (t + 3 < nt) load_k(t + 3, s3);
-    if (t + 2 < nt) load_v(t + 2, s2);
+    if (t + 2 < nt) fetch_group(t + 2);
     softmax_tile(pst(sk), t);
     phase_barrier();
     __builtin_amdgcn_s_setprio(1);
     pv_tile(vst(sk));
     if (t + 1 < nt) qk_tile(kst(sn));
+    if (t + 2 < nt) commit_group(s3, s2);
+    // Nothing is in flight here (the commit waited for its loads). Saying so
+    // unconditionally keeps the compiler's wait analysis exact across the
+    // conditional fetch/commit pair: otherwise it assumes the staging
+    // registers may still be loading at the next fetch and waits there for
+    // every load just issued.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_setprio(0);
-    if (t + 3 < nt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
   };
 
   if (nt > 0) {
-    // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)}
+    // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)} straight to LDS
     load_k(0, S0{});
     if (1 < nt) load_k(1, S1{});
     load_v(0, S0{});
@@ -540,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     phase_barrier();
     qk_tile(kst(S0{}));
     if (grp1) phase_barrier();
-    for (int64_t t = 0; t < nt; t += NS) {
+    for (int t = 0; t < nt; t += NS) {
       iteration(t, S0{});
       if (t + 1 < nt) iteration(t + 1, S1{});
       if (t + 2 < nt) iteration(t + 2, S2{});
@@ -560,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   float* lse_ptr = p.lse + (int64_t)h * lq + (r0 + li);
   if (p.accumulate) merge_weights(*lse_ptr, lse_blk, w_old, w_blk, lse_out);
   const float s_blk = w_blk * inv_l;
-  TOut* orow = (TOut*)p.o + ((r0 + li) * p.hq + h) * (int64_t)D;
+  TOut* orow = (TOut*)p.o + ((int64_t)(r0 + li) * p.hq + h) * D;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
