@@ -31,13 +31,20 @@ KERNEL_SOURCES = ("partial_fwd.hip", "device_common.hpp", "kernels.hpp")
 
 
 def kernel_source_hash():
-    """sha256 over the partial-attention kernel's sources, in a fixed order."""
+    """sha256 over the partial-attention kernel's sources, in a fixed order,
+    with comments and blank lines removed (so that a comment edit does not
+    orphan a profile taken on the same code)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "context_long_sequence_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()
 
 

@@ -31,14 +31,16 @@
 //    registers, rounded to bf16, are directly the B operand of O^T = V^T P^T.
 //    O^T keeps each lane on one query row too, so the rescale is a per-lane
 //    scalar multiply. Q stays in registers for the whole call.
-//  * K and V tiles (64 keys) go global -> LDS with buffer_load_dwordx4 ... lds
-//    (no register staging; lane offsets are loop-invariant, tile and
-//    instruction offsets are scalar) into a ring of three stages, each its
-//    own LDS array, issued a tile and a half ahead and waited for with
-//    counted vmcnt waits. Tiles are row-major with an XOR swizzle of 16-byte
-//    chunks; K is read with ds_read_b128 (rows = MFMA rows), V with
+//  * K and V tiles (64 keys) and the tile's key positions live in a ring of
+//    four LDS stages, each its own LDS array. The first load groups go
+//    global -> LDS with buffer_load_dwordx4 ... lds; in steady state each
+//    iteration fetches the next group into registers (16-byte buffer loads
+//    whose range check zero-fills rows past the block) and its matrix phase
+//    ends by writing it to LDS, because direct-to-LDS loads stall issue once
+//    a handful per CU are in flight. Tiles are row-major with an XOR swizzle
+//    of 16-byte chunks; K is read with ds_read_b128 (rows = MFMA rows), V with
 //    ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
-//    column — the V^T operand layout. The tile's key positions are staged too.
+//    column — the V^T operand layout.
 //  * Softmax runs in base 2 with the scale folded into one FMA per score.
 //    The running max is raised only when a tile's max exceeds it by more than
 //    2^8, so the O rescale is skipped on most tiles (the final normalisation
