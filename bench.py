@@ -27,7 +27,7 @@ METRIC = "causal-effective attention TFLOPS per rank share (bf16) + % of MFMA pe
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA peaks (bf16; fp32 matrix)
 
 
-KERNEL_SOURCES = ("partial_fwd.hip", "device_common.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("partial_fwd.hip", "tile_io.hpp", "device_common.hpp", "kernels.hpp")
 
 
 def kernel_source_hash():
