@@ -44,10 +44,45 @@ __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, 
   return lo;
 }
 
+// Wave-cooperative upper_bound: the first index of the ascending a[0, n) whose
+// value exceeds x. Every lane of the wave must be active and pass the same
+// arguments; the result is the same in every lane. Each round probes the last
+// element of up to 64 equal segments of the remaining range with one gather
+// and keeps the segment holding the boundary, so a search over n elements
+// takes about log64(n) + 1 dependent loads instead of log2(n).
+__device__ __forceinline__ int wave_upper_bound(const int32_t* a, int n, int32_t x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;  // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int64_t step = ((int64_t)(hi - lo) + 63) >> 6;
+    const int64_t first = (int64_t)lo + lane * step;          // this lane's segment
+    const int64_t last = imin64(first + step, (int64_t)hi) - 1;
+    const bool probe = first < hi;
+    const int32_t v = a[probe ? last : lo];
+    // segments whose last element is <= x lie wholly at or below x (a is
+    // ascending), so they are a prefix; the boundary is in the next one
+    const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(probe && v <= x));
+    const int64_t seg = (int64_t)lo + c * step;
+    if (seg >= hi) {
+      lo = hi;
+    } else {
+      hi = (int)(imin64(seg + step, (int64_t)hi) - 1);  // that segment's last element exceeds x
+      lo = (int)seg;
+    }
+  }
+  return lo;
+}
+
 // Start offset of the document holding global position p: the largest
 // cu_seqlens entry <= p (cu_seqlens is ascending, cu_seqlens[0] == 0).
 __device__ __forceinline__ int32_t doc_start(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
   int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, p) - 1;
+  return cu_seqlens[idx < 0 ? 0 : idx];
+}
+
+// doc_start for a wave-uniform position, searched by the whole wave.
+__device__ __forceinline__ int32_t wave_doc_start(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
+  const int idx = wave_upper_bound(cu_seqlens, n_seqs + 1, p) - 1;
   return cu_seqlens[idx < 0 ? 0 : idx];
 }
 

@@ -134,18 +134,24 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // ---- key range of the workgroup, and the per-wave fully visible range ----
   int kb = 0, ke = lk;                     // workgroup's visible key range
   int f_lo = 0, f_hi = lk;                 // keys every row of this wave sees
+  // (wave-cooperative searches: the positions are ascending, and a lower
+  // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
   if (p.causal) {
     int32_t wq_hi = p.q_pos[wg_r1 - 1];
-    ke = (int)upper_bound_i32(p.k_pos, lk, wq_hi);
-    if (VARLEN) kb = (int)lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]));
+    ke = wave_upper_bound(p.k_pos, lk, wq_hi);
+    if (VARLEN) kb = wave_upper_bound(p.k_pos, lk, wave_doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
     if (wave_active) {
       int32_t q_lo = p.q_pos[r0], q_hi = p.q_pos[r1 - 1];
-      f_hi = (int)upper_bound_i32(p.k_pos, lk, q_lo);
-      if (VARLEN) f_lo = (int)lower_bound_i32(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, q_hi));
+      f_hi = wave_upper_bound(p.k_pos, lk, q_lo);
+      if (VARLEN) f_lo = wave_upper_bound(p.k_pos, lk, wave_doc_start(p.cu_seqlens, p.n_seqs, q_hi) - 1);
     }
   }
   const int kt_begin = kb / BK;
   const int nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads
+  // A workgroup whose rows see none of this block's keys leaves an
+  // accumulated state exactly as it is (the merge weights are 1 and 0), so it
+  // stops here; otherwise it writes O = 0, LSE = -inf without reading Q.
+  if (nt <= 0 && p.accumulate) return;
 
   // ---- this lane's query row ----
   const int qi = min(r0 + li, lq - 1);
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // Q operand (B of S^T = K Q^T), resident in registers for the whole call.
   typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
   QReg qreg[NQ];
-  {
+  if (nt > 0) {
     const TIn* qrow = (const TIn*)p.q + ((int64_t)qi * p.hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
