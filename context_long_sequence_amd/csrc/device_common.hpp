@@ -50,18 +50,20 @@ __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, 
 // element of up to 64 equal segments of the remaining range with one gather
 // and keeps the segment holding the boundary, so a search over n elements
 // takes about log64(n) + 1 dependent loads instead of log2(n).
-__device__ __forceinline__ int wave_upper_bound(const int32_t* a, int n, int32_t x) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = n;  // the answer lies in [lo, hi]
-  while (lo < hi) {
-    const int64_t step = ((int64_t)(hi - lo) + 63) >> 6;
-    const int64_t first = (int64_t)lo + lane * step;          // this lane's segment
-    const int64_t last = imin64(first + step, (int64_t)hi) - 1;
-    const bool probe = first < hi;
-    const int32_t v = a[probe ? last : lo];
-    // segments whose last element is <= x lie wholly at or below x (a is
-    // ascending), so they are a prefix; the boundary is in the next one
-    const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(probe && v <= x));
+struct WaveSearch {
+  int lo, hi;  // the answer lies in [lo, hi]
+  int64_t step;
+  // this lane's probe: the last element of segment `lane` of [lo, hi)
+  __device__ __forceinline__ int probe_index(int lane, bool& probe) {
+    step = ((int64_t)(hi - lo) + 63) >> 6;
+    const int64_t first = (int64_t)lo + lane * step;
+    probe = first < hi;
+    return probe ? (int)(imin64(first + step, (int64_t)hi) - 1) : lo;
+  }
+  // Segments whose last element is <= x lie wholly at or below x (the array
+  // is ascending), so they are a prefix; the boundary is in the next one.
+  __device__ __forceinline__ void narrow(bool le) {
+    const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
     const int64_t seg = (int64_t)lo + c * step;
     if (seg >= hi) {
       lo = hi;
@@ -70,19 +72,43 @@ __device__ __forceinline__ int wave_upper_bound(const int32_t* a, int n, int32_t
       lo = (int)seg;
     }
   }
-  return lo;
+};
+
+__device__ __forceinline__ int wave_upper_bound(const int32_t* a, int n, int32_t x) {
+  const int lane = threadIdx.x & 63;
+  WaveSearch s{0, n, 0};
+  while (s.lo < s.hi) {
+    bool probe;
+    const int i = s.probe_index(lane, probe);
+    s.narrow(probe && a[i] <= x);
+  }
+  return s.lo;
+}
+
+// Two wave-uniform upper bounds in the same array, searched together so that
+// their rounds' loads overlap.
+__device__ __forceinline__ void wave_upper_bound2(const int32_t* a, int n, int32_t x1, int32_t x2, int& r1,
+                                                  int& r2) {
+  const int lane = threadIdx.x & 63;
+  WaveSearch s1{0, n, 0}, s2{0, n, 0};
+  while (s1.lo < s1.hi || s2.lo < s2.hi) {
+    bool p1 = false, p2 = false;
+    const bool a1 = s1.lo < s1.hi, a2 = s2.lo < s2.hi;
+    const int i1 = a1 ? s1.probe_index(lane, p1) : 0;
+    const int i2 = a2 ? s2.probe_index(lane, p2) : 0;
+    const int32_t v1 = p1 ? a[i1] : 0;
+    const int32_t v2 = p2 ? a[i2] : 0;
+    if (a1) s1.narrow(p1 && v1 <= x1);
+    if (a2) s2.narrow(p2 && v2 <= x2);
+  }
+  r1 = s1.lo;
+  r2 = s2.lo;
 }
 
 // Start offset of the document holding global position p: the largest
 // cu_seqlens entry <= p (cu_seqlens is ascending, cu_seqlens[0] == 0).
 __device__ __forceinline__ int32_t doc_start(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
   int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, p) - 1;
-  return cu_seqlens[idx < 0 ? 0 : idx];
-}
-
-// doc_start for a wave-uniform position, searched by the whole wave.
-__device__ __forceinline__ int32_t wave_doc_start(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
-  const int idx = wave_upper_bound(cu_seqlens, n_seqs + 1, p) - 1;
   return cu_seqlens[idx < 0 ? 0 : idx];
 }
 

@@ -137,13 +137,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // (wave-cooperative searches: the positions are ascending, and a lower
   // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
   if (p.causal) {
-    int32_t wq_hi = p.q_pos[wg_r1 - 1];
-    ke = wave_upper_bound(p.k_pos, lk, wq_hi);
-    if (VARLEN) kb = wave_upper_bound(p.k_pos, lk, wave_doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
-    if (wave_active) {
-      int32_t q_lo = p.q_pos[r0], q_hi = p.q_pos[r1 - 1];
-      f_hi = wave_upper_bound(p.k_pos, lk, q_lo);
-      if (VARLEN) f_lo = wave_upper_bound(p.k_pos, lk, wave_doc_start(p.cu_seqlens, p.n_seqs, q_hi) - 1);
+    // (an inactive wave, past the last row, searches with its workgroup's last row)
+    const int32_t wq_hi = p.q_pos[wg_r1 - 1];
+    const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi, q_hi = wave_active ? p.q_pos[r1 - 1] : wq_hi;
+    wave_upper_bound2(p.k_pos, lk, wq_hi, q_lo, ke, f_hi);
+    if (VARLEN) {
+      // document starts of the workgroup's first row and of the wave's last row
+      int d_wg, d_wave;
+      wave_upper_bound2(p.cu_seqlens, p.n_seqs + 1, p.q_pos[wg_r0], q_hi, d_wg, d_wave);
+      const int32_t s_wg = p.cu_seqlens[d_wg > 0 ? d_wg - 1 : 0];
+      const int32_t s_wave = p.cu_seqlens[d_wave > 0 ? d_wave - 1 : 0];
+      wave_upper_bound2(p.k_pos, lk, s_wg - 1, s_wave - 1, kb, f_lo);
     }
   }
   const int kt_begin = kb / BK;
