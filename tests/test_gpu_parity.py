@@ -129,6 +129,32 @@ def test_per_block_partials(torch_cuda, orc):
                     "%s block %d" % (name, b))
 
 
+def test_accumulate_leaves_unseeing_rows_bit_identical(torch_cuda):
+    """Folding in a block that some rows cannot see leaves those rows' (O, LSE)
+    bit-identical: their merge weights are exactly 1 (old state) and 0 (block).
+    At the reduced 64K-share shape whole workgroups see nothing of most blocks
+    and return early; the rest see it partly or wholly."""
+    from context_long_sequence_amd.share import share_from_workload
+    wl = _reduced()["c1r"]
+    share = share_from_workload(wl)
+    order = list(wl.arrival())
+    share.call_block(order[0], share.o, share.lse, accumulate=False)
+    q_pos = share.q_pos.cpu().numpy()
+    n_checked = 0
+    for b in order[1:]:
+        k_pos = share.k_pos_blocks[b].cpu().numpy()
+        blind = q_pos < k_pos.min()              # causal: these rows see no key of block b
+        o0, l0 = share.o.clone(), share.lse.clone()
+        share.call_block(b, share.o, share.lse, accumulate=True)
+        torch_cuda.cuda.synchronize()
+        rows = torch_cuda.from_numpy(np.nonzero(blind)[0]).to("cuda")
+        say("block %d: %d of %d rows see none of it" % (b, int(blind.sum()), len(blind)))
+        assert torch_cuda.equal(share.o[rows], o0[rows])
+        assert torch_cuda.equal(share.lse[:, rows], l0[:, rows])
+        n_checked += int(blind.sum())
+    assert n_checked > 0
+
+
 FULL_SAMPLES = {"c1": 512, "c2": 1024, "c3": 512, "c4": 128}
 
 
