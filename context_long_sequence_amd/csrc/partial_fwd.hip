@@ -131,12 +131,63 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int r1 = min(r0 + 32, lq);
   const bool wave_active = r0 < lq;
 
+  const int qi = min(r0 + li, lq - 1);     // this lane's query row (clamped)
+  const bool row_valid = wave_active && (r0 + li < lq);
+
+  // A workgroup whose rows see none of this block's keys leaves an
+  // accumulated state exactly as it is (the merge weights are 1 and 0), so it
+  // stops; otherwise it writes O = 0, LSE = -inf without reading Q. Keys all
+  // after the workgroup's last query is the common case, decided by one load.
+  const bool none = p.causal && (lk == 0 || p.k_pos[0] > p.q_pos[wg_r1 - 1]);
+  if (none && p.accumulate) return;
+
+  const int64_t kv_stride = (int64_t)p.hkv * D * sizeof(TIn);
+  const char* kbase = (const char*)p.k + (int64_t)hk * D * sizeof(TIn);
+  const char* vbase = (const char*)p.v + (int64_t)hk * D * sizeof(TIn);
+  const int kvoff = lane_voff<TIn, D, false, kWaves>(wave, lane, kv_stride);
+  const int vvoff = lane_voff<TIn, D, true, kWaves>(wave, lane, kv_stride);
+
+  // Q operand (B of S^T = K Q^T), resident in registers for the whole call,
+  // and, without documents, the first K/V tiles (the workgroup's keys then
+  // start at key 0): both are requested before the key-range searches, which
+  // run under their latency.
+  typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
+  QReg qreg[NQ];
+  if (!none && lk > 0) {
+    const TIn* qrow = (const TIn*)p.q + ((int64_t)qi * p.hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) {
+      if constexpr (C::kBf16) qreg[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * g);
+      else qreg[ks] = qrow[2 * ks + g];
+    }
+  }
+  // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)} of the tiles
+  // from kt0 on, straight to LDS; n_avail = tiles that exist from kt0
+  auto load_first = [&](int kt0, int n_avail) __attribute__((always_inline)) {
+    const int32_t* psrc = p.causal ? p.k_pos : (const int32_t*)p.k;
+    load_tile<TIn, D, false, kWaves>(kst(S0{}), kbase, kv_stride, kt0 * BK, lk, wave, lane, kvoff);
+    load_positions<kWaves>(pst(S0{}), psrc, kt0 * BK, lk, wave, lane);
+    if (1 < n_avail) {
+      load_tile<TIn, D, false, kWaves>(kst(S1{}), kbase, kv_stride, (kt0 + 1) * BK, lk, wave, lane, kvoff);
+      load_positions<kWaves>(pst(S1{}), psrc, (kt0 + 1) * BK, lk, wave, lane);
+    }
+    load_tile<TIn, D, true, kWaves>(vst(S0{}), vbase, kv_stride, kt0 * BK, lk, wave, lane, vvoff);
+    if (2 < n_avail) {
+      load_tile<TIn, D, false, kWaves>(kst(S2{}), kbase, kv_stride, (kt0 + 2) * BK, lk, wave, lane, kvoff);
+      load_positions<kWaves>(pst(S2{}), psrc, (kt0 + 2) * BK, lk, wave, lane);
+    }
+    if (1 < n_avail)
+      load_tile<TIn, D, true, kWaves>(vst(S1{}), vbase, kv_stride, (kt0 + 1) * BK, lk, wave, lane, vvoff);
+  };
+  const bool early = !VARLEN && !none && lk > 0;
+  if (early) load_first(0, (lk + BK - 1) / BK);  // (tiles past the workgroup's range go unread)
+
   // ---- key range of the workgroup, and the per-wave fully visible range ----
   int kb = 0, ke = lk;                     // workgroup's visible key range
   int f_lo = 0, f_hi = lk;                 // keys every row of this wave sees
   // (wave-cooperative searches: the positions are ascending, and a lower
   // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
-  if (p.causal) {
+  if (p.causal && !none) {
     // (an inactive wave, past the last row, searches with its workgroup's last row)
     const int32_t wq_hi = p.q_pos[wg_r1 - 1];
     const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi, q_hi = wave_active ? p.q_pos[r1 - 1] : wq_hi;
@@ -150,30 +201,18 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       wave_upper_bound2(p.k_pos, lk, s_wg - 1, s_wave - 1, kb, f_lo);
     }
   }
+  if (none) ke = 0;
   const int kt_begin = kb / BK;
-  const int nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads
-  // A workgroup whose rows see none of this block's keys leaves an
-  // accumulated state exactly as it is (the merge weights are 1 and 0), so it
-  // stops here; otherwise it writes O = 0, LSE = -inf without reading Q.
-  if (nt <= 0 && p.accumulate) return;
+  const int nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads (>= 1 when early)
+  // (with documents the rows may still see nothing; tiles are loaded early only
+  // without documents, where nt >= 1, but never leave with loads into LDS in flight)
+  if (nt <= 0 && p.accumulate) {
+    if (early) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    return;
+  }
 
-  // ---- this lane's query row ----
-  const int qi = min(r0 + li, lq - 1);
-  const bool row_valid = wave_active && (r0 + li < lq);
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
   const int32_t my_start = (VARLEN && p.causal) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
-
-  // Q operand (B of S^T = K Q^T), resident in registers for the whole call.
-  typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
-  QReg qreg[NQ];
-  if (nt > 0) {
-    const TIn* qrow = (const TIn*)p.q + ((int64_t)qi * p.hq + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < NQ; ++ks) {
-      if constexpr (C::kBf16) qreg[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * g);
-      else qreg[ks] = qrow[2 * ks + g];
-    }
-  }
 
   f32x16_t oacc[NDT];
 #pragma unroll
@@ -181,21 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   float m_run = neg_inf();  // running max of scale*log2(e)*score (may lag the true max by < kTau)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  const int64_t kv_stride = (int64_t)p.hkv * D * sizeof(TIn);
-  const char* kbase = (const char*)p.k + (int64_t)hk * D * sizeof(TIn);
-  const char* vbase = (const char*)p.v + (int64_t)hk * D * sizeof(TIn);
-
   // ---- loads: group G(t) = {K(t+1) and its positions, V(t)}; tile t lives in stage t % NS ----
-  const int kvoff = lane_voff<TIn, D, false, kWaves>(wave, lane, kv_stride);
-  const int vvoff = lane_voff<TIn, D, true, kWaves>(wave, lane, kv_stride);
-  auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
-    const int j0 = (kt_begin + t) * BK;
-    load_tile<TIn, D, false, kWaves>(kst(st), kbase, kv_stride, j0, lk, wave, lane, kvoff);
-    load_positions<kWaves>(pst(st), p.causal ? p.k_pos : (const int32_t*)p.k, j0, lk, wave, lane);
-  };
-  auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
-    load_tile<TIn, D, true, kWaves>(vst(st), vbase, kv_stride, (kt_begin + t) * BK, lk, wave, lane, vvoff);
-  };
   // steady state: G(j) is fetched into registers one period ahead, then committed to its stages
   u32x4_t kreg[C::kInst / kWaves], vreg[C::kInst / kWaves];
   int32_t preg = 0;
@@ -428,12 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   };
 
   if (nt > 0) {
-    // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)} straight to LDS
-    load_k(0, S0{});
-    if (1 < nt) load_k(1, S1{});
-    load_v(0, S0{});
-    if (2 < nt) load_k(2, S2{});
-    if (1 < nt) load_v(1, S1{});
+    if (!early) load_first(kt_begin, nt);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
     qk_tile(kst(S0{}));
