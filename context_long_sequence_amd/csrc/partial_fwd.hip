@@ -49,6 +49,13 @@
 //    only tiles it does not see in full (tiles it cannot see at all are
 //    computed and fully masked: within a workgroup's range that is at most a
 //    tile or two per wave near a diagonal or a document start).
+//  * Workgroup start is latency-bound (a few dependent memory round trips
+//    before the first MFMA), so it is kept short: a workgroup that cannot see
+//    the block is recognised from its first key alone and, when
+//    accumulating, leaves at once (the merge would not change its state);
+//    the key-range bounds are found by the whole wave, 64 probes per round,
+//    the workgroup's and the wave's in the same rounds; and without
+//    documents Q and the first three tiles are requested before the searches.
 //  * Workgroup ids are remapped so that consecutive logical tiles (same KV
 //    head) run on the same XCD and share its L2; heavy (late-position) query
 //    tiles are scheduled first.
