@@ -91,6 +91,10 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain elementwise copy of MIB MiB (read once, written "
                          "once) a few times: the reference kernel that scales the HBM byte counters")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="instead of the headline line, measure the KV arrival pipeline on the workload "
+                         "(communication alone, computation alone, overlapped) for pieces of 1K..8K keys "
+                         "delivered from pinned host memory and from device memory; one JSON line each")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -125,6 +129,10 @@ def main():
     pairs = visible_pairs(share.q_pos_host, share.k_pos_host, qs)
     flops_blocks = [4.0 * wl.d * wl.hq * p for p in pairs]
     step_flops = sum(flops_blocks)
+
+    if args.pipeline:
+        pipeline_sweep(wl, share, order, step_flops)
+        return
 
     for _ in range(args.warmup):
         share.step(order)
@@ -199,6 +207,29 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, share, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def pipeline_sweep(wl, share, order, step_flops, chunks=(1024, 2048, 4096, 8192), slots=3, reps=3):
+    """The arrival pipeline of the FCP page's overlap section: KV pieces of
+    `chunk` keys copied in on one stream while the kernels fold them in on
+    another, one event per piece each way. Prints one JSON line per (source,
+    chunk): communication alone, computation alone, overlapped (ms per step)
+    and the fraction of the shorter side the overlap hid."""
+    from context_long_sequence_amd.pipeline import ArrivalPipeline
+    kv_bytes = sum(2 * k.numel() * k.element_size() + p.numel() * 4
+                   for k, p in zip(share.k_blocks, share.k_pos_blocks))
+    for source in ("host", "device"):
+        for chunk in chunks:
+            pipe = ArrivalPipeline(share, chunk, n_slots=slots, source=source)
+            m = pipe.measure(order, reps=reps, warmup=1)
+            m.update({"metric": "KV arrival pipeline: overlapped step time", "unit": "ms",
+                      "higher_is_better": False, "workload": wl.name,
+                      "link_GBps": kv_bytes / (m["comm_ms"] * 1e-3) / 1e9,
+                      "overlapped_TFLOPs": step_flops / (m["overlapped_ms"] * 1e-3) / 1e12})
+            print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}), flush=True)
+            log("pipeline %s chunk %d: comm %.3f ms, compute %.3f ms, overlapped %.3f ms, hidden %.2f" % (
+                source, chunk, m["comm_ms"], m["compute_ms"], m["overlapped_ms"], m["hidden"]))
+            del pipe
 
 
 def calibrate_copy(mib, reps=5):
