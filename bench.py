@@ -95,6 +95,9 @@ def main():
                     help="instead of the headline line, measure the KV arrival pipeline on the workload "
                          "(communication alone, computation alone, overlapped) for pieces of 1K..8K keys "
                          "delivered from pinned host memory and from device memory; one JSON line each")
+    ap.add_argument("--fused", action="store_true",
+                    help="instead of the headline line, time the step as ONE cpattn_partial_multi call over all "
+                         "blocks (state kept in registers between blocks); one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -132,6 +135,9 @@ def main():
 
     if args.pipeline:
         pipeline_sweep(wl, share, order, step_flops)
+        return
+    if args.fused:
+        fused_step(wl, share, order, step_flops, args.steps, args.warmup)
         return
 
     for _ in range(args.warmup):
@@ -207,6 +213,29 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, share, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def fused_step(wl, share, order, step_flops, steps, warmup):
+    """The step as one multi-block call (the FCP page's blocks arriving
+    together): prints one JSON line in the headline's unit."""
+    import torch
+    for _ in range(warmup):
+        share.step(order, "fused")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        share.step(order, "fused")
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    tflops = step_flops / (ms * 1e-3) / 1e12
+    log("fused step: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
+    print(json.dumps({"metric": METRIC + ", one multi-block call per step", "value": round(tflops, 2),
+                      "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+                      "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
+                      "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
 
 
 def pipeline_sweep(wl, share, order, step_flops, chunks=(1024, 2048, 4096, 8192), slots=3, reps=3):

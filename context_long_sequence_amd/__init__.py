@@ -10,6 +10,8 @@ Functions (same names as the C ABI):
   cpattn_zigzag_index(total_len, cp_size, rank, layout, cu_seqlens=None)
   cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0, accumulate=False)
   cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_scale=0.0, accumulate=False)
+  cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,
+                       accumulate=False, cu_seqlens=None)
   cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
 
 Layouts: q, o [lq, hq, d]; k, v [lk, hkv, d]; lse [hq, lq] float32; positions
@@ -64,6 +66,9 @@ def load_library(path=LIB_PATH):
     lib.cpattn_varlen_partial.restype = ctypes.c_int
     lib.cpattn_varlen_partial.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32, f32,
                                           vp, ctypes.c_int, vp, i32, vp]
+    lib.cpattn_partial_multi.restype = ctypes.c_int
+    lib.cpattn_partial_multi.argtypes = [vp, vp, vp, ctypes.c_int, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32,
+                                         i32, f32, vp, ctypes.c_int, vp, i32, vp]
     lib.cpattn_merge_lse.restype = ctypes.c_int
     lib.cpattn_merge_lse.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp]
     if path == LIB_PATH:
@@ -171,6 +176,36 @@ def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_sca
     _check(lib, st)
 
 
+def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,
+                         accumulate=False, cu_seqlens=None, stream=None):
+    """Fold several arrived KV blocks into (o, lse) in one launch, in list
+    order; see cpattn_partial_multi in include/cpattn.h."""
+    import torch
+    lib = load_library()
+    n = len(k_blocks)
+    if n == 0 or len(v_blocks) != n or len(k_pos_blocks) != n:
+        raise CpattnError(5, "k_blocks, v_blocks and k_pos_blocks must be non-empty lists of one length")
+    for k, v in zip(k_blocks, v_blocks):
+        _shapes(q, k, o, lse)
+        if tuple(v.shape) != tuple(k.shape):
+            raise CpattnError(2, "each v must have its k's shape")
+    ptrs = ctypes.c_void_p * n
+    kp = ptrs(*[_dev(k, "k", q.dtype) for k in k_blocks])
+    vp_ = ptrs(*[_dev(v, "v", q.dtype) for v in v_blocks])
+    pp = ptrs(*[_dev(p, "k_pos", torch.int32) for p in k_pos_blocks])
+    lks = (ctypes.c_int64 * n)(*[int(k.shape[0]) for k in k_blocks])
+    lq, hq, d = q.shape
+    hkv = k_blocks[0].shape[1]
+    st = lib.cpattn_partial_multi(_dev(q, "q"), ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp_, ctypes.c_void_p),
+                                  _dtype_code(q), lq, ctypes.cast(lks, ctypes.c_void_p), n, hq, hkv, d,
+                                  _dev(q_pos, "q_pos", torch.int32), ctypes.cast(pp, ctypes.c_void_p),
+                                  _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                                  0 if cu_seqlens is None else cu_seqlens.numel() - 1, int(bool(causal)),
+                                  float(softmax_scale), _dev(o, "o"), _dtype_code(o), _dev(lse, "lse", torch.float32),
+                                  int(bool(accumulate)), _stream(stream))
+    _check(lib, st)
+
+
 def cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part, stream=None):
     """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
     import torch
@@ -186,5 +221,6 @@ def cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part, stream=None):
     _check(lib, st)
 
 
-__all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_merge_lse", "cpattn_version",
+__all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_partial_multi",
+           "cpattn_merge_lse", "cpattn_version",
            "CpattnError", "load_library", "header_functions"]

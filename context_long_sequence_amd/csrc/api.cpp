@@ -127,6 +127,42 @@ cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpatt
   return ok();
 }
 
+cpattn_status enqueue_partial_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                                    cpattn_dtype in_dtype, int64_t lq, const int64_t* lk_blocks, int32_t n_blocks,
+                                    int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                    const int32_t* const* k_pos_blocks, const int32_t* cu_seqlens, int32_t n_seqs,
+                                    int32_t causal, float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse,
+                                    int32_t accumulate, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_env() && causal) {
+    cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
+    for (int32_t b = 0; b < n_blocks && st == CPATTN_OK; ++b)
+      st = check_sorted_device(k_pos_blocks[b], lk_blocks[b], "k_pos", s);
+    if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
+    if (st != CPATTN_OK) return st;
+  }
+  if (lq == 0) return ok();
+  cpattn::PartialParams p{};
+  p.q = q; p.k = k_blocks[0]; p.v = v_blocks[0]; p.o = o; p.lse = lse;
+  p.q_pos = q_pos; p.k_pos = k_pos_blocks[0]; p.cu_seqlens = cu_seqlens; p.n_seqs = n_seqs;
+  p.lq = lq; p.lk = lk_blocks[0]; p.hq = hq; p.hkv = hkv;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal; p.accumulate = accumulate;
+  cpattn::BlockTable bt{};
+  bt.n = n_blocks;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    bt.k[b] = k_blocks[b];
+    bt.v[b] = v_blocks[b];
+    bt.k_pos[b] = k_pos_blocks[b];
+    bt.lk[b] = (int32_t)lk_blocks[b];
+  }
+  hipError_t e = cpattn::launch_partial_multi(p, bt, in_dtype == CPATTN_BF16, o_dtype == CPATTN_BF16, head_dim,
+                                              cu_seqlens != nullptr, s);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +248,32 @@ cpattn_status cpattn_varlen_partial(const void* q, const void* k, const void* v,
   if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
   return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, cu_seqlens, n_seqs, 1,
                          softmax_scale, o, o_dtype, lse, accumulate, stream);
+}
+
+cpattn_status cpattn_partial_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                                   cpattn_dtype in_dtype, int64_t lq, const int64_t* lk_blocks, int32_t n_blocks,
+                                   int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                   const int32_t* const* k_pos_blocks, const int32_t* cu_seqlens, int32_t n_seqs,
+                                   int32_t causal, float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse,
+                                   int32_t accumulate, void* stream) {
+  if (!k_blocks || !v_blocks || !lk_blocks || !k_pos_blocks)
+    return fail(CPATTN_ERR_NULL, "the block arrays must be non-NULL");
+  if (n_blocks < 1 || n_blocks > cpattn::kMaxBlocks)
+    return fail(CPATTN_ERR_RANGE, "n_blocks must be in [1, %d], got %d", cpattn::kMaxBlocks, n_blocks);
+  if (cu_seqlens) {
+    if (causal != 1) return fail(CPATTN_ERR_RANGE, "documents (cu_seqlens) need causal = 1");
+    if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+    if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  }
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    cpattn_status st = check_partial_args(q, k_blocks[b], v_blocks[b], in_dtype, lq, lk_blocks[b], hq, hkv,
+                                          head_dim, q_pos, k_pos_blocks[b], causal, o, o_dtype, lse, accumulate);
+    if (st != CPATTN_OK) return st;
+  }
+  if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
+  return enqueue_partial_multi(q, k_blocks, v_blocks, in_dtype, lq, lk_blocks, n_blocks, hq, hkv, head_dim, q_pos,
+                               k_pos_blocks, cu_seqlens, cu_seqlens ? n_seqs : 0, causal, softmax_scale, o, o_dtype,
+                               lse, accumulate, stream);
 }
 
 cpattn_status cpattn_merge_lse(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,

@@ -25,8 +25,22 @@ struct PartialParams {
   int32_t causal, accumulate;
 };
 
+// The KV blocks of a multi-block call (passed by value as a kernel argument).
+constexpr int kMaxBlocks = 32;
+struct BlockTable {
+  int32_t n;
+  int32_t lk[kMaxBlocks];
+  const void* k[kMaxBlocks];
+  const void* v[kMaxBlocks];
+  const int32_t* k_pos[kMaxBlocks];
+};
+
 // Enqueue the partial-attention kernel; arguments are already validated.
 hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_dim, bool varlen, hipStream_t stream);
+
+// Enqueue the kernel over the blocks of `bt` in order (p's k, v, k_pos, lk unused).
+hipError_t launch_partial_multi(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
+                                bool varlen, hipStream_t stream);
 
 // Enqueue the standalone merge (o_acc, lse_acc) <- merge(acc, part).
 hipError_t launch_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part, int out_bf16,

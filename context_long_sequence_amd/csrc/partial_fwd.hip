@@ -72,8 +72,8 @@ namespace cpattn {
 constexpr int kWaves = 8;                 // two groups of four
 constexpr int kThreads = kWaves * 64;
 
-template <typename TIn, typename TOut, int D, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams p) {
+template <typename TIn, typename TOut, int D, bool VARLEN, bool MULTI>
+__global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams p, BlockTable bt) {
   using C = Cfg<TIn, D, kWaves>;
   constexpr int NB = C::kNB;
   constexpr int BK = C::kBK;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
 
   // row and key indices fit in 32 bits (the host checks lq, lk < 2^31), which
   // keeps the tile bookkeeping on the scalar unit
-  const int lq = (int)p.lq, lk = (int)p.lk;
+  const int lq = (int)p.lq;
   const int wg_r0 = qt * 32 * p.r_wg;
   const int wg_r1 = min(wg_r0 + 32 * p.r_wg, lq);
   const int r0 = wg_r0 + 32 * rb;
@@ -141,37 +141,53 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int qi = min(r0 + li, lq - 1);     // this lane's query row (clamped)
   const bool row_valid = wave_active && (r0 + li < lq);
 
-  // A workgroup whose rows see none of this block's keys leaves an
-  // accumulated state exactly as it is (the merge weights are 1 and 0), so it
-  // stops; otherwise it writes O = 0, LSE = -inf without reading Q. Keys all
-  // after the workgroup's last query is the common case, decided by one load.
-  const bool none = p.causal && (lk == 0 || p.k_pos[0] > p.q_pos[wg_r1 - 1]);
-  if (none && p.accumulate) return;
-
   const int64_t kv_stride = (int64_t)p.hkv * D * sizeof(TIn);
-  const char* kbase = (const char*)p.k + (int64_t)hk * D * sizeof(TIn);
-  const char* vbase = (const char*)p.v + (int64_t)hk * D * sizeof(TIn);
   const int kvoff = lane_voff<TIn, D, false, kWaves>(wave, lane, kv_stride);
   const int vvoff = lane_voff<TIn, D, true, kWaves>(wave, lane, kv_stride);
 
+  // ---- the block being folded in ----
+  // A single-block call folds in p's block; a multi-block call the blocks of
+  // the table one after the other, with the running state kept in registers
+  // between them. These are set at the top of each block.
+  const void* kraw = p.k;                 // the block's key tensor
+  const char* kbase = nullptr;            // its K and V rows of this KV head
+  const char* vbase = nullptr;
+  const int32_t* kpos = p.k_pos;          // its key positions
+  int lk = 0;                             // its keys
+  int kt_begin = 0, nt = 0;               // the workgroup's first tile and tile count
+  int f_lo = 0, f_hi = 0;                 // keys every row of this wave sees
+  auto set_block = [&](int blk) __attribute__((always_inline)) {
+    const void* vraw = p.v;
+    lk = (int)p.lk;
+    if constexpr (MULTI) {
+      kraw = bt.k[blk];
+      vraw = bt.v[blk];
+      kpos = bt.k_pos[blk];
+      lk = bt.lk[blk];
+    }
+    kbase = (const char*)kraw + (int64_t)hk * D * sizeof(TIn);
+    vbase = (const char*)vraw + (int64_t)hk * D * sizeof(TIn);
+  };
+
   // Q operand (B of S^T = K Q^T), resident in registers for the whole call,
-  // and, without documents, the first K/V tiles (the workgroup's keys then
-  // start at key 0): both are requested before the key-range searches, which
-  // run under their latency.
+  // loaded once, with the first block the workgroup sees anything of.
   typedef typename std::conditional<C::kBf16, bf16x8_t, float>::type QReg;
   QReg qreg[NQ];
-  if (!none && lk > 0) {
+  bool q_loaded = false;
+  auto load_q = [&]() __attribute__((always_inline)) {
+    if (q_loaded) return;
     const TIn* qrow = (const TIn*)p.q + ((int64_t)qi * p.hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       if constexpr (C::kBf16) qreg[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * g);
       else qreg[ks] = qrow[2 * ks + g];
     }
-  }
+    q_loaded = true;
+  };
   // G(-1) = {K(0)}, G(0) = {K(1), V(0)}, G(1) = {K(2), V(1)} of the tiles
   // from kt0 on, straight to LDS; n_avail = tiles that exist from kt0
   auto load_first = [&](int kt0, int n_avail) __attribute__((always_inline)) {
-    const int32_t* psrc = p.causal ? p.k_pos : (const int32_t*)p.k;
+    const int32_t* psrc = p.causal ? kpos : (const int32_t*)kraw;
     load_tile<TIn, D, false, kWaves>(kst(S0{}), kbase, kv_stride, kt0 * BK, lk, wave, lane, kvoff);
     load_positions<kWaves>(pst(S0{}), psrc, kt0 * BK, lk, wave, lane);
     if (1 < n_avail) {
@@ -186,37 +202,6 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     if (1 < n_avail)
       load_tile<TIn, D, true, kWaves>(vst(S1{}), vbase, kv_stride, (kt0 + 1) * BK, lk, wave, lane, vvoff);
   };
-  const bool early = !VARLEN && !none && lk > 0;
-  if (early) load_first(0, (lk + BK - 1) / BK);  // (tiles past the workgroup's range go unread)
-
-  // ---- key range of the workgroup, and the per-wave fully visible range ----
-  int kb = 0, ke = lk;                     // workgroup's visible key range
-  int f_lo = 0, f_hi = lk;                 // keys every row of this wave sees
-  // (wave-cooperative searches: the positions are ascending, and a lower
-  // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
-  if (p.causal && !none) {
-    // (an inactive wave, past the last row, searches with its workgroup's last row)
-    const int32_t wq_hi = p.q_pos[wg_r1 - 1];
-    const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi, q_hi = wave_active ? p.q_pos[r1 - 1] : wq_hi;
-    wave_upper_bound2(p.k_pos, lk, wq_hi, q_lo, ke, f_hi);
-    if (VARLEN) {
-      // document starts of the workgroup's first row and of the wave's last row
-      int d_wg, d_wave;
-      wave_upper_bound2(p.cu_seqlens, p.n_seqs + 1, p.q_pos[wg_r0], q_hi, d_wg, d_wave);
-      const int32_t s_wg = p.cu_seqlens[d_wg > 0 ? d_wg - 1 : 0];
-      const int32_t s_wave = p.cu_seqlens[d_wave > 0 ? d_wave - 1 : 0];
-      wave_upper_bound2(p.k_pos, lk, s_wg - 1, s_wave - 1, kb, f_lo);
-    }
-  }
-  if (none) ke = 0;
-  const int kt_begin = kb / BK;
-  const int nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads (>= 1 when early)
-  // (with documents the rows may still see nothing; tiles are loaded early only
-  // without documents, where nt >= 1, but never leave with loads into LDS in flight)
-  if (nt <= 0 && p.accumulate) {
-    if (early) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    return;
-  }
 
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
   const int32_t my_start = (VARLEN && p.causal) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
@@ -235,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   auto fetch_group = [&](int j) __attribute__((always_inline)) {  // requires j < nt
     const int j0 = (kt_begin + j) * BK;
     fetch_tile<TIn, D, kWaves>(kreg, kbase, (int)kv_stride, j0 + BK, lk, wave, kvoff);
-    preg = fetch_positions<kWaves>(p.causal ? p.k_pos : nullptr, j0 + BK, lk, wave, lane);
+    preg = fetch_positions<kWaves>(p.causal ? kpos : nullptr, j0 + BK, lk, wave, lane);
     fetch_tile<TIn, D, kWaves>(vreg, vbase, (int)kv_stride, j0, lk, wave, vvoff);
   };
   auto commit_group = [&](auto sk1, auto sv) __attribute__((always_inline)) {
@@ -459,7 +444,55 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     phase_barrier();
   };
 
-  if (nt > 0) {
+  bool seen = false;  // the workgroup saw some key of some block
+  for (int blk = 0; blk < (MULTI ? bt.n : 1); ++blk) {
+    set_block(blk);
+    // Rows that see none of a block's keys: when accumulating, a single-block
+    // call leaves the state exactly as it is (the merge weights would be 1
+    // and 0), so the workgroup stops here; otherwise the block is skipped.
+    // Keys all after the workgroup's last query is the common case, decided
+    // by one load before any search.
+    const bool none = p.causal && (lk == 0 || kpos[0] > p.q_pos[wg_r1 - 1]);
+    if (none || lk <= 0) {
+      if (!MULTI && p.accumulate) return;
+      continue;
+    }
+    // Q and, without documents, the first K/V tiles (the workgroup's keys
+    // then start at key 0) are requested before the key-range searches,
+    // which run under their latency.
+    load_q();
+    const bool early = !VARLEN;
+    if (early) load_first(0, (lk + BK - 1) / BK);  // (tiles past the workgroup's range go unread)
+
+    // ---- key range of the workgroup, and the per-wave fully visible range ----
+    // (wave-cooperative searches: the positions are ascending, and a lower
+    // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
+    int kb = 0, ke = lk;
+    f_lo = 0;
+    f_hi = lk;
+    if (p.causal) {
+      // (an inactive wave, past the last row, searches with its workgroup's last row)
+      const int32_t wq_hi = p.q_pos[wg_r1 - 1];
+      const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi, q_hi = wave_active ? p.q_pos[r1 - 1] : wq_hi;
+      wave_upper_bound2(kpos, lk, wq_hi, q_lo, ke, f_hi);
+      if (VARLEN) {
+        // document starts of the workgroup's first row and of the wave's last row
+        int d_wg, d_wave;
+        wave_upper_bound2(p.cu_seqlens, p.n_seqs + 1, p.q_pos[wg_r0], q_hi, d_wg, d_wave);
+        const int32_t s_wg = p.cu_seqlens[d_wg > 0 ? d_wg - 1 : 0];
+        const int32_t s_wave = p.cu_seqlens[d_wave > 0 ? d_wave - 1 : 0];
+        wave_upper_bound2(kpos, lk, s_wg - 1, s_wave - 1, kb, f_lo);
+      }
+    }
+    kt_begin = kb / BK;
+    nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads (>= 1 without documents)
+    if (nt <= 0) {
+      // (with documents the rows may still see nothing; tiles are loaded early
+      // only without documents, but never leave with loads into LDS in flight)
+      if (early) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      continue;
+    }
+    seen = true;
     if (!early) load_first(kt_begin, nt);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
@@ -471,8 +504,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       if (t + 2 < nt) iteration(t + 2, S2{});
       if (t + 3 < nt) iteration(t + 3, S3{});
     }
+    // (after this barrier no wave reads the ring, so the next block may refill it)
     if (!grp1) phase_barrier();
   }
+  if (!seen && p.accumulate) return;
 
   // ---- finalise: O = acc / l, LSE = ln(l) + max; merge into the stored state if accumulating ----
   const float l_tot = half_swap_sum(l_run);
@@ -518,14 +553,21 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
 // ---------------------------------------------------------------------------
 
 template <typename TIn, typename TOut, int D>
-static hipError_t launch_typed(const PartialParams& p, bool varlen, hipStream_t stream) {
+static hipError_t launch_typed(const PartialParams& p, const BlockTable& bt, bool varlen, bool multi,
+                               hipStream_t stream) {
   dim3 grid(p.n_wg), block(kThreads);
-  if (varlen) hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, true>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, false>), grid, block, 0, stream, p);
+  if (multi) {
+    if (varlen) hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, true, true>), grid, block, 0, stream, p, bt);
+    else hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, false, true>), grid, block, 0, stream, p, bt);
+  } else {
+    if (varlen) hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, true, false>), grid, block, 0, stream, p, bt);
+    else hipLaunchKernelGGL((partial_fwd_kernel<TIn, TOut, D, false, false>), grid, block, 0, stream, p, bt);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_dim, bool varlen, hipStream_t stream) {
+static hipError_t launch_any(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
+                             bool varlen, bool multi, hipStream_t stream) {
   // a workgroup: g_wg query heads of one KV group x r_wg blocks of 32 rows, g_wg * r_wg = kWaves
   const int G = p.hq / p.hkv;
   p.g_wg = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
@@ -537,13 +579,24 @@ hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_d
   if (n_wg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   p.n_wg = (int32_t)n_wg;
   if (in_bf16) {
-    if (head_dim == 128) return out_bf16 ? launch_typed<__bf16, __bf16, 128>(p, varlen, stream)
-                                         : launch_typed<__bf16, float, 128>(p, varlen, stream);
-    return out_bf16 ? launch_typed<__bf16, __bf16, 64>(p, varlen, stream)
-                    : launch_typed<__bf16, float, 64>(p, varlen, stream);
+    if (head_dim == 128) return out_bf16 ? launch_typed<__bf16, __bf16, 128>(p, bt, varlen, multi, stream)
+                                         : launch_typed<__bf16, float, 128>(p, bt, varlen, multi, stream);
+    return out_bf16 ? launch_typed<__bf16, __bf16, 64>(p, bt, varlen, multi, stream)
+                    : launch_typed<__bf16, float, 64>(p, bt, varlen, multi, stream);
   }
-  if (head_dim == 128) return launch_typed<float, float, 128>(p, varlen, stream);
-  return launch_typed<float, float, 64>(p, varlen, stream);
+  if (head_dim == 128) return launch_typed<float, float, 128>(p, bt, varlen, multi, stream);
+  return launch_typed<float, float, 64>(p, bt, varlen, multi, stream);
+}
+
+hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_dim, bool varlen, hipStream_t stream) {
+  BlockTable bt{};
+  bt.n = 1;
+  return launch_any(p, bt, in_bf16, out_bf16, head_dim, varlen, false, stream);
+}
+
+hipError_t launch_partial_multi(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
+                                bool varlen, hipStream_t stream) {
+  return launch_any(p, bt, in_bf16, out_bf16, head_dim, varlen, true, stream);
 }
 
 }  // namespace cpattn

@@ -8,7 +8,7 @@ the C ABI. This is the loop of the FCP page ("ä»Žå›ºå®šçŽ¯åˆ°è‡ªç”±æ‹“æ‰‘ï¼šFCPå
 """
 import numpy as np
 
-from . import cpattn_merge_lse, cpattn_partial, cpattn_varlen_partial, cpattn_zigzag_index
+from . import cpattn_merge_lse, cpattn_partial, cpattn_partial_multi, cpattn_varlen_partial, cpattn_zigzag_index
 
 
 def bits_to_device(a, device="cuda"):
@@ -63,15 +63,26 @@ class RankShare:
             cpattn_partial(self.q, self.k_blocks[b], self.v_blocks[b], self.q_pos, self.k_pos_blocks[b], o, lse,
                            causal=self.causal, accumulate=accumulate)
 
+    def call_multi(self, blocks, o, lse, accumulate):
+        blocks = list(blocks)
+        cpattn_partial_multi(self.q, [self.k_blocks[b] for b in blocks], [self.v_blocks[b] for b in blocks],
+                             self.q_pos, [self.k_pos_blocks[b] for b in blocks], o, lse, causal=self.causal,
+                             accumulate=accumulate, cu_seqlens=self.cu_seqlens)
+
     def step(self, order, mode="accumulate"):
         """Fold every block, in `order`, into (self.o, self.lse) and return them.
 
         mode 'accumulate': the kernel merges each block in its epilogue.
         mode 'merge': each block is written as its own partial, then merged by
         the standalone merge kernel.
+        mode 'fused': all blocks in one cpattn_partial_multi call (the state
+        stays in registers between blocks).
         """
         import torch
         order = list(order)
+        if mode == "fused":
+            self.call_multi(order, self.o, self.lse, accumulate=False)
+            return self.o, self.lse
         self.call_block(order[0], self.o, self.lse, accumulate=False)
         if mode == "accumulate":
             for b in order[1:]:

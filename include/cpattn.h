@@ -142,6 +142,32 @@ cpattn_status cpattn_varlen_partial(const void *q, const void *k, const void *v,
                                     void *o, cpattn_dtype o_dtype, float *lse, int32_t accumulate, void *stream);
 
 /*
+ * Several KV blocks that have all arrived, folded into (o, lse) in ONE launch
+ * (the FCP page, §3.3: blocks may arrive together and in any order). The
+ * result is that of cpattn_partial (cpattn_varlen_partial when cu_seqlens is
+ * non-NULL) called on each block in the given order, up to rounding: the
+ * running maximum, running sum and the unnormalised O stay in registers
+ * between blocks, so O is rounded and written once instead of once per block
+ * (and the state of the rows is read once when accumulate = 1).
+ *
+ *  k_blocks, v_blocks, k_pos_blocks  HOST arrays of n_blocks DEVICE pointers:
+ *                     block b is k_blocks[b], v_blocks[b] [lk_blocks[b]][hkv][head_dim]
+ *                     and its ascending key positions k_pos_blocks[b] [lk_blocks[b]]
+ *  lk_blocks          HOST array of n_blocks lengths (each in [0, 2^31))
+ *  n_blocks           1..32
+ *  cu_seqlens, n_seqs documents as in cpattn_varlen_partial (causal must be 1), or NULL / 0
+ * Every other argument is as in cpattn_partial; each block is checked as a
+ * cpattn_partial call would check it. The caller keeps ownership of every
+ * buffer; the host arrays are read before the call returns.
+ */
+cpattn_status cpattn_partial_multi(const void *q, const void *const *k_blocks, const void *const *v_blocks,
+                                   cpattn_dtype in_dtype, int64_t lq, const int64_t *lk_blocks, int32_t n_blocks,
+                                   int32_t hq, int32_t hkv, int32_t head_dim, const int32_t *q_pos,
+                                   const int32_t *const *k_pos_blocks, const int32_t *cu_seqlens, int32_t n_seqs,
+                                   int32_t causal, float softmax_scale, void *o, cpattn_dtype o_dtype, float *lse,
+                                   int32_t accumulate, void *stream);
+
+/*
  * In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part)),
  * the exact combination of two partial results over disjoint key sets (the
  * global max / global sum normaliser of the PCP page, §4.2, taken two shards

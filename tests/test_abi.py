@@ -16,7 +16,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = cp.header_functions()
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
-                          "cpattn_varlen_partial", "cpattn_merge_lse"}
+                          "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -84,6 +84,35 @@ def test_varlen_and_merge_reject(lib):
     assert lib.cpattn_merge_lse(O, L, C, P, 7, 8, 1, 64, 0) == STATUS["ERR_DTYPE"]
     assert lib.cpattn_merge_lse(O, L, O + 16, P, 0, 8, 1, 64, 0) == STATUS["ERR_ALIAS"]
     assert lib.cpattn_merge_lse(O + 8, L, C, P, 0, 8, 1, 64, 0) == STATUS["ERR_ALIGN"]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+def test_multi_rejects(lib):
+    import ctypes
+
+    def arr(t, vals):
+        a = (t * len(vals))(*vals)
+        return a, ctypes.cast(a, ctypes.c_void_p).value
+
+    kb, kbp = arr(ctypes.c_void_p, [B, B + 0x1000])
+    vb, vbp = arr(ctypes.c_void_p, [C, C + 0x1000])
+    pb, pbp = arr(ctypes.c_void_p, [K, K + 0x1000])
+    lk, lkp = arr(ctypes.c_int64, [8, 8])
+
+    def call(n=2, k=kbp, lks=lkp, hd=64, cu=0, ns=0, causal=1, o=O, acc=0):
+        return lib.cpattn_partial_multi(A, k, vbp, 0, 8, lks, n, 1, 1, hd, P, pbp, cu, ns, causal, 0.0, o, 0, L,
+                                        acc, 0)
+    assert call(k=0) == STATUS["ERR_NULL"]                    # no block array
+    assert call(n=0) == STATUS["ERR_RANGE"]                   # no block
+    assert call(n=33) == STATUS["ERR_RANGE"]                  # over the table size
+    assert call(hd=80) == STATUS["ERR_SHAPE"]                 # checked per block as cpattn_partial would
+    assert call(cu=0x80000, ns=1, causal=0) == STATUS["ERR_RANGE"]   # documents need causal
+    assert call(cu=0x80002, ns=1) == STATUS["ERR_ALIGN"]
+    assert call(cu=0x80000, ns=0) == STATUS["ERR_SHAPE"]
+    bad_lk, bad_lkp = arr(ctypes.c_int64, [8, 1 << 31])
+    assert call(lks=bad_lkp) == STATUS["ERR_SHAPE"]           # the second block's length
+    assert call(o=B + 0x1000 + 16) == STATUS["ERR_ALIAS"]     # o overlaps the second block's k
+    assert call(acc=2) == STATUS["ERR_RANGE"]
 
 
 def test_last_error_is_thread_local(lib):
