@@ -59,6 +59,10 @@
 //  * Workgroup ids are remapped so that consecutive logical tiles (same KV
 //    head) run on the same XCD and share its L2; heavy (late-position) query
 //    tiles are scheduled first.
+//  * A multi-block call (several blocks that have all arrived) runs the same
+//    code in a loop over a table of blocks: each block gets its own
+//    emptiness test, searches and tile loop, while the running max, running
+//    sum and unnormalised O stay in registers, so O is written once.
 //  * Float32 inputs use the same skeleton with v_mfma_f32_32x32x2_f32 and
 //    32-key tiles.
 #include <type_traits>
