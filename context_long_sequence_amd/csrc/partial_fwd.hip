@@ -217,20 +217,32 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   float l_run = 0.f;        // this lane's share of the running sum
 
   // ---- loads: group G(t) = {K(t+1) and its positions, V(t)}; tile t lives in stage t % NS ----
-  // steady state: G(j) is fetched into registers one period ahead, then committed to its stages
-  u32x4_t kreg[C::kInst / kWaves], vreg[C::kInst / kWaves];
-  int32_t preg = 0;
-  // (for j = nt-1 the K part reads nothing and writes zeros to a free stage)
-  auto fetch_group = [&](int j) __attribute__((always_inline)) {  // requires j < nt
+  // steady state: G(j) is fetched into registers ahead, then committed to its stages.
+  // With d = 64 a tile's period is half as long, too short to cover the load
+  // latency of a key range that streams from memory, and registers are to
+  // spare: G(j) is then fetched two periods ahead into staging set j % 2.
+  constexpr bool kDeep = C::kBf16 && D == 64;
+  constexpr int NSET = kDeep ? 2 : 1;
+  u32x4_t kreg[NSET][C::kInst / kWaves], vreg[NSET][C::kInst / kWaves];
+  int32_t preg[NSET] = {};
+  // Rows past `lim` read nothing (zeros). The one-ahead fetch is issued only
+  // for j < nt (for j = nt-1 the K part is past the range: zeros written to a
+  // free stage); the two-ahead fetch is unconditional, so that the compiler's
+  // count of loads in flight is the same on every path, and is all zeros for
+  // groups past the workgroup's tiles.
+  auto fetch_group = [&](int j, auto set) __attribute__((always_inline)) {
+    constexpr int e = decltype(set)::value;
     const int j0 = (kt_begin + j) * BK;
-    fetch_tile<TIn, D, kWaves>(kreg, kbase, (int)kv_stride, j0 + BK, lk, wave, kvoff);
-    preg = fetch_positions<kWaves>(p.causal ? kpos : nullptr, j0 + BK, lk, wave, lane);
-    fetch_tile<TIn, D, kWaves>(vreg, vbase, (int)kv_stride, j0, lk, wave, vvoff);
+    const int klim = (!kDeep || j + 1 < nt) ? lk : 0, vlim = (!kDeep || j < nt) ? lk : 0;
+    fetch_tile<TIn, D, kWaves>(kreg[e], kbase, (int)kv_stride, j0 + BK, klim, wave, kvoff);
+    preg[e] = fetch_positions<kWaves>(p.causal ? kpos : nullptr, j0 + BK, klim, wave, lane);
+    fetch_tile<TIn, D, kWaves>(vreg[e], vbase, (int)kv_stride, j0, vlim, wave, vvoff);
   };
-  auto commit_group = [&](auto sk1, auto sv) __attribute__((always_inline)) {
-    commit_tile<TIn, D, kWaves>(kst(sk1), kreg, wave, lane);
-    commit_positions<kWaves>(pst(sk1), preg, wave, lane);
-    commit_tile<TIn, D, kWaves>(vst(sv), vreg, wave, lane);
+  auto commit_group = [&](auto sk1, auto sv, auto set) __attribute__((always_inline)) {
+    constexpr int e = decltype(set)::value;
+    commit_tile<TIn, D, kWaves>(kst(sk1), kreg[e], wave, lane);
+    commit_positions<kWaves>(pst(sk1), preg[e], wave, lane);
+    commit_tile<TIn, D, kWaves>(vst(sv), vreg[e], wave, lane);
   };
 
   // does every row of this wave see every key of tile t?
@@ -431,21 +443,36 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     const std::integral_constant<int, (k + 1) % NS> sn{};
     const std::integral_constant<int, (k + 2) % NS> s2{};
     const std::integral_constant<int, (k + 3) % NS> s3{};
-    if (t + 2 < nt) fetch_group(t + 2);
-    softmax_tile(pst(sk), t);
-    phase_barrier();
-    __builtin_amdgcn_s_setprio(1);
-    pv_tile(vst(sk));
-    if (t + 1 < nt) qk_tile(kst(sn));
-    if (t + 2 < nt) commit_group(s3, s2);
-    // Nothing is in flight here (the commit waited for its loads). Saying so
-    // unconditionally keeps the compiler's wait analysis exact across the
-    // conditional fetch/commit pair: otherwise it assumes the staging
-    // registers may still be loading at the next fetch and waits there for
-    // every load just issued.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_setprio(0);
-    phase_barrier();
+    if constexpr (kDeep) {
+      // fetch G(t+3) into set (t+3) % 2, commit G(t+2) from set (t+2) % 2
+      // (t = k mod 4, so the parities are compile-time constants)
+      fetch_group(t + 3, std::integral_constant<int, (k + 3) & 1>{});
+      softmax_tile(pst(sk), t);
+      phase_barrier();
+      __builtin_amdgcn_s_setprio(1);
+      pv_tile(vst(sk));
+      if (t + 1 < nt) qk_tile(kst(sn));
+      commit_group(s3, s2, std::integral_constant<int, (k + 2) & 1>{});  // (zeros past the tiles, into free stages)
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+    } else {
+      const std::integral_constant<int, 0> set0{};
+      if (t + 2 < nt) fetch_group(t + 2, set0);
+      softmax_tile(pst(sk), t);
+      phase_barrier();
+      __builtin_amdgcn_s_setprio(1);
+      pv_tile(vst(sk));
+      if (t + 1 < nt) qk_tile(kst(sn));
+      if (t + 2 < nt) commit_group(s3, s2, set0);
+      // Nothing is in flight here (the commit waited for its loads). Saying so
+      // unconditionally keeps the compiler's wait analysis exact across the
+      // conditional fetch/commit pair: otherwise it assumes the staging
+      // registers may still be loading at the next fetch and waits there for
+      // every load just issued.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+    }
   };
 
   bool seen = false;  // the workgroup saw some key of some block
@@ -500,6 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     if (!early) load_first(kt_begin, nt);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
+    if constexpr (kDeep) fetch_group(2, std::integral_constant<int, 0>{});  // G(2), committed in iteration 0
     qk_tile(kst(S0{}));
     if (grp1) phase_barrier();
     for (int t = 0; t < nt; t += NS) {

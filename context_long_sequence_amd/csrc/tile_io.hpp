@@ -143,13 +143,17 @@ __device__ __forceinline__ void load_positions(int32_t CPATTN_LDS* kp_tile, cons
 // per-lane offset, which the range check sees.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// n (wave-uniform) clamped to [0, hi]. The clamp is selected as a vector
-// instruction (v_med3); reading the result back as a scalar keeps the buffer
-// descriptor built from it in scalar registers (a descriptor the compiler
-// thinks may vary per lane costs a loop over lanes at every load).
+// n (wave-uniform) clamped to [0, hi], on the scalar unit. Written as plain
+// min/max the clamp is selected as a vector instruction (v_med3) whose result
+// is read back with readfirstlane: that needs a vector register for a moment,
+// and the compiler picks one of the staging registers, which can make it wait
+// for every load in flight. The result must stay scalar anyway (a buffer
+// descriptor the compiler thinks may vary per lane costs a loop over lanes at
+// every load).
 __device__ __forceinline__ int clamp_rows(int n, int hi) {
-  n = n < hi ? n : hi;
-  return __builtin_amdgcn_readfirstlane(n > 0 ? n : 0);
+  int r;
+  asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(n), "s"(hi));
+  return r;
 }
 
 template <typename TIn, int D, int NW>
