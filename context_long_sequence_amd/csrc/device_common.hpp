@@ -85,6 +85,37 @@ __device__ __forceinline__ int wave_upper_bound(const int32_t* a, int n, int32_t
   return s.lo;
 }
 
+// N wave-uniform upper bounds, search i in the ascending a[i][0, n[i]) for
+// x[i], all searched together so that their rounds' loads overlap.
+template <int N>
+__device__ __forceinline__ void wave_upper_bounds(const int32_t* const (&a)[N], const int (&n)[N],
+                                                  const int32_t (&x)[N], int (&r)[N]) {
+  const int lane = threadIdx.x & 63;
+  WaveSearch s[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) s[i] = WaveSearch{0, n[i], 0};
+  for (;;) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) any = any || s[i].lo < s[i].hi;
+    if (!any) break;
+    bool act[N], pr[N];
+    int32_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      act[i] = s[i].lo < s[i].hi;
+      pr[i] = false;
+      const int idx = act[i] ? s[i].probe_index(lane, pr[i]) : 0;
+      v[i] = pr[i] ? a[i][idx] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (act[i]) s[i].narrow(pr[i] && v[i] <= x[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) r[i] = s[i].lo;
+}
+
 // Two wave-uniform upper bounds in the same array, searched together so that
 // their rounds' loads overlap.
 __device__ __forceinline__ void wave_upper_bound2(const int32_t* a, int n, int32_t x1, int32_t x2, int& r1,

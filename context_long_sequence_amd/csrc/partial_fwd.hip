@@ -208,7 +208,27 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   };
 
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
-  const int32_t my_start = (VARLEN && p.causal) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
+  // Documents (the same for every block): the starts of the documents of the
+  // workgroup's first row and of the wave's last row, and this lane's own. The
+  // three document indices are searched together; when the wave's first and
+  // last rows share a document (nearly always) every lane's start is that
+  // document's, and only a wave across a document boundary searches per lane.
+  int32_t s_wg = 0, s_wave = 0, my_start = 0;
+  if constexpr (VARLEN) {
+    if (p.causal) {
+      const int32_t wq_lo = p.q_pos[wg_r0];
+      const int32_t q_first = wave_active ? p.q_pos[r0] : p.q_pos[wg_r1 - 1];
+      const int32_t q_last = wave_active ? p.q_pos[r1 - 1] : p.q_pos[wg_r1 - 1];
+      int d[3];
+      const int32_t* const cus[3] = {p.cu_seqlens, p.cu_seqlens, p.cu_seqlens};
+      const int ns[3] = {p.n_seqs + 1, p.n_seqs + 1, p.n_seqs + 1};
+      const int32_t xs[3] = {wq_lo, q_first, q_last};
+      wave_upper_bounds<3>(cus, ns, xs, d);
+      s_wg = p.cu_seqlens[d[0] > 0 ? d[0] - 1 : 0];
+      s_wave = p.cu_seqlens[d[2] > 0 ? d[2] - 1 : 0];
+      my_start = d[1] == d[2] ? s_wave : doc_start(p.cu_seqlens, p.n_seqs, my_qpos);
+    }
+  }
 
   f32x16_t oacc[NDT];
 #pragma unroll
@@ -504,15 +524,20 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     if (p.causal) {
       // (an inactive wave, past the last row, searches with its workgroup's last row)
       const int32_t wq_hi = p.q_pos[wg_r1 - 1];
-      const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi, q_hi = wave_active ? p.q_pos[r1 - 1] : wq_hi;
-      wave_upper_bound2(kpos, lk, wq_hi, q_lo, ke, f_hi);
-      if (VARLEN) {
-        // document starts of the workgroup's first row and of the wave's last row
-        int d_wg, d_wave;
-        wave_upper_bound2(p.cu_seqlens, p.n_seqs + 1, p.q_pos[wg_r0], q_hi, d_wg, d_wave);
-        const int32_t s_wg = p.cu_seqlens[d_wg > 0 ? d_wg - 1 : 0];
-        const int32_t s_wave = p.cu_seqlens[d_wave > 0 ? d_wave - 1 : 0];
-        wave_upper_bound2(kpos, lk, s_wg - 1, s_wave - 1, kb, f_lo);
+      const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi;
+      if constexpr (VARLEN) {
+        // both ends of both ranges in the same rounds (the document starts are known)
+        int r[4];
+        const int32_t* const ks[4] = {kpos, kpos, kpos, kpos};
+        const int ns[4] = {lk, lk, lk, lk};
+        const int32_t xs[4] = {wq_hi, q_lo, s_wg - 1, s_wave - 1};
+        wave_upper_bounds<4>(ks, ns, xs, r);
+        ke = r[0];
+        f_hi = r[1];
+        kb = r[2];
+        f_lo = r[3];
+      } else {
+        wave_upper_bound2(kpos, lk, wq_hi, q_lo, ke, f_hi);
       }
     }
     kt_begin = kb / BK;
