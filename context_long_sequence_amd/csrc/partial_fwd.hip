@@ -571,40 +571,84 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const bool empty = !(l_tot > 0.f);
   const float inv_l = empty ? 0.f : 1.0f / l_tot;
   const float lse_blk = empty ? neg_inf() : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  if (!row_valid) return;
 
   float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
   float* lse_ptr = p.lse + (int64_t)h * lq + (r0 + li);
-  if (p.accumulate) merge_weights(*lse_ptr, lse_blk, w_old, w_blk, lse_out);
+  if (p.accumulate && row_valid) merge_weights(*lse_ptr, lse_blk, w_old, w_blk, lse_out);
   const float s_blk = w_blk * inv_l;
-  TOut* orow = (TOut*)p.o + ((int64_t)(r0 + li) * p.hq + h) * D;
+  if constexpr (sizeof(TOut) == 2) {
+    // bf16 O goes out through LDS, which no wave reads any more: each lane
+    // holds 4-column pieces of one row, so writing them straight out would
+    // cover each 128-byte line of O with eight partial writes; staged as
+    // rows, every store instruction writes whole lines (16 bytes a lane, the
+    // lanes of a row side by side). Each wave stages its own 32 rows in one
+    // stage array (row stride padded by 16 bytes against bank conflicts);
+    // LDS operations of one wave complete in order.
+    constexpr int RS = D * 2 + 16;           // staged row stride (bytes)
+    constexpr int CH = D * 2 / 16;           // 16-byte chunks per row
+    constexpr int RPP = 64 / CH;             // rows per pass of the wave
+    static_assert(32 * RS <= TB, "a wave's rows fit in one stage array");
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    char CPATTN_LDS* stg = wave < 4 ? (wave == 0 ? kst(S0{}) : wave == 1 ? kst(S1{}) : wave == 2 ? kst(S2{}) : kst(S3{}))
+                                    : (wave == 4 ? vst(S0{}) : wave == 5 ? vst(S1{}) : wave == 6 ? vst(S2{}) : vst(S3{}));
+    TOut* obase = (TOut*)p.o + ((int64_t)r0 * p.hq + h) * D;  // row r0 of this wave's head
+    const int64_t ostride = (int64_t)p.hq * D;                 // elements from one row to the next
+    const int n_rows = wave_active ? min(32, lq - r0) : 0;
+    const int prow = lane / CH, pchunk = lane % CH;            // this lane's place in a pass
+    if (p.accumulate) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int row = pass * RPP + prow;
+        if (row < n_rows)
+          *(u32x4 CPATTN_LDS*)(stg + row * RS + pchunk * 16) = *(const u32x4*)(obase + row * ostride + pchunk * 8);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int dv = 32 * dt + 8 * rr + 4 * g;
-      float v0 = oacc[dt][4 * rr] * s_blk, v1 = oacc[dt][4 * rr + 1] * s_blk;
-      float v2 = oacc[dt][4 * rr + 2] * s_blk, v3 = oacc[dt][4 * rr + 3] * s_blk;
-      if constexpr (sizeof(TOut) == 2) {
-        uint2* dst = (uint2*)(orow + dv);
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int dv = 32 * dt + 8 * rr + 4 * g;
+        float v0 = oacc[dt][4 * rr] * s_blk, v1 = oacc[dt][4 * rr + 1] * s_blk;
+        float v2 = oacc[dt][4 * rr + 2] * s_blk, v3 = oacc[dt][4 * rr + 3] * s_blk;
+        u32x2 CPATTN_LDS* slot = (u32x2 CPATTN_LDS*)(stg + li * RS + dv * 2);
         if (p.accumulate) {
-          uint2 old = *dst;
+          const u32x2 old = *slot;
           v0 += w_old * bf16_bits_to_f32((uint16_t)(old.x & 0xFFFF));
           v1 += w_old * bf16_bits_to_f32((uint16_t)(old.x >> 16));
           v2 += w_old * bf16_bits_to_f32((uint16_t)(old.y & 0xFFFF));
           v3 += w_old * bf16_bits_to_f32((uint16_t)(old.y >> 16));
         }
-        *dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-      } else {
-        float4* dst = (float4*)(orow + dv);
-        if (p.accumulate) {
-          float4 old = *dst;
-          v0 += w_old * old.x; v1 += w_old * old.y; v2 += w_old * old.z; v3 += w_old * old.w;
-        }
-        *dst = make_float4(v0, v1, v2, v3);
+        *slot = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int row = pass * RPP + prow;
+      if (row < n_rows)
+        *(u32x4*)(obase + row * ostride + pchunk * 8) = *(const u32x4 CPATTN_LDS*)(stg + row * RS + pchunk * 16);
     }
-  if (g == 0) *lse_ptr = lse_out;
+  } else {
+    if (row_valid) {
+      TOut* orow = (TOut*)p.o + ((int64_t)(r0 + li) * p.hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int dv = 32 * dt + 8 * rr + 4 * g;
+          float v0 = oacc[dt][4 * rr] * s_blk, v1 = oacc[dt][4 * rr + 1] * s_blk;
+          float v2 = oacc[dt][4 * rr + 2] * s_blk, v3 = oacc[dt][4 * rr + 3] * s_blk;
+          float4* dst = (float4*)(orow + dv);
+          if (p.accumulate) {
+            float4 old = *dst;
+            v0 += w_old * old.x; v1 += w_old * old.y; v2 += w_old * old.z; v3 += w_old * old.w;
+          }
+          *dst = make_float4(v0, v1, v2, v3);
+        }
+    }
+  }
+  if (g == 0 && row_valid) *lse_ptr = lse_out;
 }
 
 // ---------------------------------------------------------------------------
