@@ -16,6 +16,9 @@ all arithmetic is fp64. Functions and the passages they follow:
   the blockwise method must equal full attention).
 * ``merge`` — the exact combination of two partial results (PCP page §4.2,
   FCP page §3.3).
+* ``attention_grad`` — dQ, dK, dV of ``attention`` for a given dO, from the
+  definition of softmax attention (the backward that training-time context
+  parallelism runs over the same blocks, PCP page §2.3).
 
 Nothing here is parity-unpinned: ``tests/test_oracle.py`` pins every function
 (brute force at 50 digits, closed forms, invariants, the pages' literal index
@@ -71,6 +74,12 @@ class Oracle:
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_double,
                                            ctypes.c_int64, ctypes.c_int32, _f64p]
+        lib.oracle_attention_grad.restype = ctypes.c_int
+        lib.oracle_attention_grad.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_double,
+                                              _f64p, _i64p, _i32p, ctypes.c_int64, _f64p, _f64p, _f64p, _f64p,
+                                              ctypes.c_int32]
         lib.oracle_merge.restype = None
         lib.oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p]
         self.lib = lib
@@ -150,6 +159,52 @@ class Oracle:
         if n < 0:
             raise ValueError("oracle_softmax_row rejected its arguments")
         return p
+
+    # -- gradients -----------------------------------------------------------
+    def attention_grad(self, q, k, v, dout, q_pos=None, k_pos=None, q_start=None, causal=True, scale=None,
+                       rows=None, heads=None, n_threads=0):
+        """Gradients of ``attention`` for the output gradient dout [lq, hq, d].
+
+        Without rows/heads: returns (dq [lq, hq, d], dk [lk, hkv, d],
+        dv [lk, hkv, d], delta [lq, hq]). With rows/heads: (dq [n, d], None,
+        None, delta [n]) for those (row, head) pairs only.
+        """
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        code = _dtype_code(q)
+        assert _dtype_code(k) == code and _dtype_code(v) == code
+        lq, hq, d = q.shape
+        lk, hkv, _ = k.shape
+        dout = np.ascontiguousarray(dout, np.float64)
+        assert dout.shape == q.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        qp = None if q_pos is None else np.ascontiguousarray(q_pos, np.int32)
+        kp = None if k_pos is None else np.ascontiguousarray(k_pos, np.int32)
+        qs = None if q_start is None else np.ascontiguousarray(q_start, np.int32)
+        if rows is None:
+            r = h = None
+            n = lq * hq
+            dk = np.zeros((lk, hkv, d), np.float64)
+            dv = np.zeros((lk, hkv, d), np.float64)
+        else:
+            r = np.ascontiguousarray(rows, np.int64)
+            h = np.ascontiguousarray(heads, np.int32)
+            n = len(r)
+            dk = dv = None
+        dq = np.zeros((n, d), np.float64)
+        delta = np.zeros(n, np.float64)
+        rc = self.lib.oracle_attention_grad(q.ctypes.data, k.ctypes.data, v.ctypes.data, code, lq, lk, hq, hkv, d,
+                                            _ptr(qp, _i32p), _ptr(qs, _i32p), _ptr(kp, _i32p), int(bool(causal)),
+                                            float(scale), _ptr(dout, _f64p), _ptr(r, _i64p), _ptr(h, _i32p), n,
+                                            _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p), _ptr(delta, _f64p),
+                                            int(n_threads))
+        if rc != 0:
+            raise ValueError("oracle_attention_grad rejected its arguments")
+        if rows is None:
+            return dq.reshape(lq, hq, d), dk, dv, delta.reshape(lq, hq)
+        return dq, None, None, delta
 
     # -- merge ---------------------------------------------------------------
     def merge(self, o_a, lse_a, o_b, lse_b):

@@ -236,3 +236,148 @@ void oracle_merge(int64_t n_rows, int32_t d,
         lse_out[n] = L;
     }
 }
+
+/* ---- gradients of the attention above --------------------------------- */
+
+/* The backward pass that training-time context parallelism runs after the
+ * forward (PCP page §2.3: the backward exchanges the same blocks again; Halo
+ * page, Ulysses section: heads stay independent). For a loss with gradient dO
+ * with respect to O, everything follows from the definition
+ *     O_i = sum_j P_ij v_j,  P_ij = exp(s_ij) / sum_j' exp(s_ij'),  s_ij = scale <q_i, k_j>
+ * over the keys visible to row i:
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = <dO_i, v_j>
+ *     dS_ij = P_ij (dP_ij - D_i),  D_i = sum_j P_ij dP_ij = <dO_i, O_i>
+ *     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+ * where the sums for dK and dV also run over every query head that reads the
+ * key's KV head. A row with no visible key contributes nothing.
+ *
+ * Pass 1 (per (row, head) pair): scores, max, normaliser, O_i, D_i, dQ_i.
+ * Pass 2 (per (key, KV head)): dK_j and dV_j from every visible (row, head),
+ * with P recomputed from the row's normaliser. */
+int oracle_attention_grad(const void *q, const void *k, const void *v, int32_t in_dtype,
+                          int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t d,
+                          const int32_t *q_pos, const int32_t *q_start, const int32_t *k_pos,
+                          int32_t causal, double scale, const double *dout,
+                          const int64_t *rows, const int32_t *heads, int64_t n_pairs,
+                          double *dq, double *dk, double *dv, double *delta, int32_t n_threads) {
+    if (!q || !k || !v || !dout || hq < 1 || hkv < 1 || hq % hkv || d < 1 || lq < 0 || lk < 0) return -1;
+    if (causal && (!q_pos || !k_pos)) return -1;
+    if ((rows == NULL) != (heads == NULL)) return -1;
+    if (rows && (dk || dv)) return -1;          /* key gradients need every row */
+    if (!rows) n_pairs = lq * hq;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    /* per pair: ln of the normaliser (m + ln l) and D, kept for pass 2 */
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+    double *dd = (double *)malloc(sizeof(double) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+    if (!lse || !dd) {
+        free(lse);
+        free(dd);
+        return -1;
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(lk > 0 ? lk : 1));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow || !orow) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < n_pairs; ++n) {
+            if (!s || !qrow || !orow) continue;
+            int64_t i = rows ? rows[n] : n / hq;
+            int32_t h = heads ? heads[n] : (int32_t)(n % hq);
+            if (i < 0 || i >= lq || h < 0 || h >= hq) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            int32_t g = h / (hq / hkv);
+            const double *dorow = dout + (i * hq + h) * (int64_t)d;
+            double m;
+            int64_t count = score_row(q, k, in_dtype, lk, hq, hkv, d, q_pos, q_start, k_pos,
+                                      causal, scale, i, h, qrow, s, &m);
+            if (dq)
+                for (int32_t t = 0; t < d; ++t) dq[n * d + t] = 0.0;
+            if (count == 0) {            /* sees nothing: no gradient flows through this row */
+                lse[n] = -INFINITY;
+                dd[n] = 0.0;
+                if (delta) delta[n] = 0.0;
+                continue;
+            }
+            double z = 0.0;              /* the row's normaliser, relative to its max */
+            for (int64_t j = 0; j < lk; ++j)
+                if (s[j] != -INFINITY) z += exp(s[j] - m);
+            /* O_i and D_i = <dO_i, O_i> */
+            for (int32_t t = 0; t < d; ++t) orow[t] = 0.0;
+            for (int64_t j = 0; j < lk; ++j) {
+                if (s[j] == -INFINITY) continue;
+                double p = exp(s[j] - m) / z;
+                int64_t kv = (j * hkv + g) * (int64_t)d;   /* row j of KV head g */
+                for (int32_t t = 0; t < d; ++t) orow[t] += p * load_value(v, in_dtype, kv + t);
+            }
+            double di = 0.0;
+            for (int32_t t = 0; t < d; ++t) di += dorow[t] * orow[t];
+            lse[n] = m + log(z);
+            dd[n] = di;
+            if (delta) delta[n] = di;
+            if (!dq) continue;
+            /* dQ_i = scale sum_j P_ij (<dO_i, v_j> - D_i) k_j */
+            for (int64_t j = 0; j < lk; ++j) {
+                if (s[j] == -INFINITY) continue;
+                double p = exp(s[j] - m) / z;
+                int64_t kv = (j * hkv + g) * (int64_t)d;
+                double dp = 0.0;
+                for (int32_t t = 0; t < d; ++t) dp += dorow[t] * load_value(v, in_dtype, kv + t);
+                double ds = p * (dp - di);
+                for (int32_t t = 0; t < d; ++t) dq[n * d + t] += scale * ds * load_value(k, in_dtype, kv + t);
+            }
+        }
+        free(s);
+        free(qrow);
+        free(orow);
+    }
+    if (!failed && (dk || dv)) {
+        int32_t group = hq / hkv;
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t jg = 0; jg < lk * hkv; ++jg) {
+            int64_t j = jg / hkv;
+            int32_t g = (int32_t)(jg % hkv);
+            double *dkj = dk ? dk + jg * d : NULL;
+            double *dvj = dv ? dv + jg * d : NULL;
+            for (int32_t t = 0; t < d; ++t) {
+                if (dkj) dkj[t] = 0.0;
+                if (dvj) dvj[t] = 0.0;
+            }
+            for (int32_t h = g * group; h < (g + 1) * group; ++h) {
+                for (int64_t i = 0; i < lq; ++i) {
+                    if (!key_visible(causal, q_pos ? q_pos[i] : 0, q_start, i, k_pos ? k_pos[j] : 0)) continue;
+                    int64_t n = i * hq + h;
+                    if (lse[n] == -INFINITY) continue;
+                    double acc = 0.0, dp = 0.0;
+                    const double *dorow = dout + n * (int64_t)d;
+                    for (int32_t t = 0; t < d; ++t) {
+                        acc += load_value(q, in_dtype, n * (int64_t)d + t) * load_value(k, in_dtype, jg * d + t);
+                        dp += dorow[t] * load_value(v, in_dtype, jg * d + t);
+                    }
+                    double p = exp(scale * acc - lse[n]);
+                    double ds = p * (dp - dd[n]);
+                    for (int32_t t = 0; t < d; ++t) {
+                        if (dkj) dkj[t] += scale * ds * load_value(q, in_dtype, n * (int64_t)d + t);
+                        if (dvj) dvj[t] += p * dorow[t];
+                    }
+                }
+            }
+        }
+    }
+    free(lse);
+    free(dd);
+    return failed ? -1 : 0;
+}

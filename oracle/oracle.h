@@ -17,6 +17,9 @@
  *  [HALO]   "长上下文训练 256k 不难：Halo 上下文并行（CP + Ulysses 注意力）原理与实测"
  *           (sheratonhq.com), Ulysses section — heads are independent, grouped
  *           KV heads are shared without copying.
+ *  The gradients (oracle_attention_grad) are those of the same definition:
+ *  the backward pass that training with context parallelism runs over the
+ *  same KV blocks ([PCP] §2.3).
  *
  * Everything is the plain definition: scores in fp64 from the exact input
  * values, a max pass, a sum pass, a weighted-sum pass. No tiling, no online
@@ -75,6 +78,22 @@ void oracle_merge(int64_t n_rows, int32_t d,
                   const double *o_a, const double *lse_a,
                   const double *o_b, const double *lse_b,
                   double *o_out, double *lse_out);
+
+/* Gradients of the attention above for a loss whose gradient with respect to
+ * O is dout ([lq][hq][d], fp64). Masking, GQA and dtype as oracle_attention.
+ * rows/heads == NULL: every (i, h), in order i*hq + h, and dk, dv (nullable,
+ * [lk][hkv][d]) receive the key gradients summed over the query heads of each
+ * KV head. With a rows/heads list only dq (and delta) of those pairs are
+ * computed; dk and dv must then be NULL.
+ * dq (nullable): [n_pairs][d]; delta (nullable): [n_pairs], D = <dO, O>.
+ * A pair with no visible key gets dq = 0 and delta = 0.
+ * Returns 0, or -1 on bad arguments. */
+int oracle_attention_grad(const void *q, const void *k, const void *v, int32_t in_dtype,
+                          int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t d,
+                          const int32_t *q_pos, const int32_t *q_start, const int32_t *k_pos,
+                          int32_t causal, double scale, const double *dout,
+                          const int64_t *rows, const int32_t *heads, int64_t n_pairs,
+                          double *dq, double *dk, double *dv, double *delta, int32_t n_threads);
 
 #ifdef __cplusplus
 }

@@ -48,14 +48,19 @@ def _vals(a):
 
 def attention(q, k, v, q_pos, k_pos, q_start=None, causal=True, scale=None):
     """Dense attention; returns (o[i][h][t], lse[i][h]) as mpmath numbers."""
-    Q, K, V = _vals(q), _vals(k), _vals(v)
+    return attention_values(_vals(q), _vals(k), _vals(v), q_pos, k_pos, q_start, causal, scale)
+
+
+def attention_values(Q, K, V, q_pos, k_pos, q_start=None, causal=True, scale=None, only_rows=None):
+    """Dense attention of nested lists Q[i][h][t], K[j][g][t], V[j][g][t]
+    (numbers or mpf); `only_rows` limits the computed query rows (others None)."""
     lq, hq, d = len(Q), len(Q[0]), len(Q[0][0])
     lk, hkv = len(K), len(K[0])
     scale = mpmath.mpf(1) / mpmath.sqrt(d) if scale is None else mpmath.mpf(scale)
     group = hq // hkv
     o = [[None] * hq for _ in range(lq)]
     lse = [[None] * hq for _ in range(lq)]
-    for i in range(lq):
+    for i in (range(lq) if only_rows is None else only_rows):
         for h in range(hq):
             g = h // group
             weights, rows = [], []
@@ -77,3 +82,44 @@ def attention(q, k, v, q_pos, k_pos, q_start=None, causal=True, scale=None):
                        for t in range(d)]
             lse[i][h] = mpmath.log(Z)
     return o, lse
+
+
+def grad_fd(q, k, v, dout, q_pos, k_pos, q_start=None, causal=True, scale=None, step="1e-15"):
+    """Gradients of loss = sum dout * O with respect to q, k, v by central
+    differences of ``attention_values`` at 50 digits (truncation error of
+    order step^2, far below fp64 rounding). Returns nested lists of mpf:
+    dq[i][h][t], dk[j][g][t], dv[j][g][t]."""
+    Q, K, V = _vals(q), _vals(k), _vals(v)
+    dO = dout.tolist()
+    hstep = mpmath.mpf(step)
+    lq, hq, d = len(Q), len(Q[0]), len(Q[0][0])
+    lk, hkv = len(K), len(K[0])
+
+    def loss(Qx, Kx, Vx, rows=None):
+        o, _ = attention_values(Qx, Kx, Vx, q_pos, k_pos, q_start, causal, scale, rows)
+        return mpmath.fsum(mpmath.mpf(dO[i][h][t]) * o[i][h][t]
+                           for i in (range(lq) if rows is None else rows) for h in range(hq) for t in range(d))
+
+    def perturbed(X, idx, delta):
+        Y = [[list(r) for r in m] for m in X]
+        a, b, c = idx
+        Y[a][b][c] = mpmath.mpf(Y[a][b][c]) + delta
+        return Y
+
+    dq = [[[None] * d for _ in range(hq)] for _ in range(lq)]
+    for i in range(lq):             # q_i only moves row i's output
+        for h in range(hq):
+            for t in range(d):
+                up = loss(perturbed(Q, (i, h, t), hstep), K, V, [i])
+                dn = loss(perturbed(Q, (i, h, t), -hstep), K, V, [i])
+                dq[i][h][t] = (up - dn) / (2 * hstep)
+    dk = [[[None] * d for _ in range(hkv)] for _ in range(lk)]
+    dv = [[[None] * d for _ in range(hkv)] for _ in range(lk)]
+    for j in range(lk):
+        for g in range(hkv):
+            for t in range(d):
+                dk[j][g][t] = (loss(Q, perturbed(K, (j, g, t), hstep), V)
+                               - loss(Q, perturbed(K, (j, g, t), -hstep), V)) / (2 * hstep)
+                dv[j][g][t] = (loss(Q, K, perturbed(V, (j, g, t), hstep))
+                               - loss(Q, K, perturbed(V, (j, g, t), -hstep))) / (2 * hstep)
+    return dq, dk, dv

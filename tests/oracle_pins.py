@@ -9,6 +9,10 @@ the oracle disagrees with:
     heads and the Ulysses head split of the Halo page),
   * the pages' literal index facts (the striped example and the split
     arithmetic) and closed-form pair counts.
+  * for the gradients: central differences at 50 digits of the brute-force
+    forward, the zero-sum and sum-to-dO invariants of dK and dV, invariance
+    under a common key shift, GQA = repeated heads, and closed forms (one
+    visible key per row, Q = 0).
 
 ``tests/test_oracle.py`` runs them on the real oracle; ``tests/test_oracle_mutants.py``
 runs them on copies of the oracle with planted mistakes and requires each
@@ -356,5 +360,140 @@ def pin_index_maps(orc):
         raise AssertionError("non-divisible split must be rejected: %s" % (bad,))
 
 
+# ---------------------------------------------------------------------------
+# 7. gradients: 50-digit finite differences of the brute-force forward
+
+GRAD_CASES = [
+    # (S, cp, rank, layout, hq, hkv, d, dtype, doc_lens, key_ranks, causal)
+    (8, 2, 1, "zigzag", 2, 1, 3, "bf16", None, "all", True),      # GQA, diagonal and off-diagonal keys
+    (16, 2, 0, "zigzag", 1, 1, 2, "f32", (4, 8, 4), "all", True),  # documents
+    (16, 4, 0, "zigzag", 2, 2, 2, "bf16", None, (1, 2), True),     # some rows see none of these keys
+    (8, 2, 0, "contiguous", 2, 1, 3, "f32", None, (1,), False),    # no mask
+]
+
+
+def _grad_case(orc, case_i, case):
+    S, cp, r, layout, hq, hkv, d, dtype, docs, key_ranks, causal = case
+    seed = 500 + case_i
+    if docs is None:
+        qp, _ = orc.local_positions(S, cp, r, layout)
+        bq, bqs, qs = brute.rank_tokens(S, cp, r, layout), None, None
+    else:
+        qp, qs = orc.local_positions(S, cp, r, layout, doc_lens=list(docs))
+        bq, bqs = brute.rank_tokens_docs(docs, cp, r, layout)
+    ranks = range(cp) if key_ranks == "all" else key_ranks
+    kp, bk = [], []
+    for kr in ranks:
+        if docs is None:
+            kp.append(orc.local_positions(S, cp, kr, layout)[0])
+            bk += brute.rank_tokens(S, cp, kr, layout)
+        else:
+            kp.append(orc.local_positions(S, cp, kr, layout, doc_lens=list(docs))[0])
+            bk += brute.rank_tokens_docs(docs, cp, kr, layout)[0]
+    kp = np.concatenate(kp)
+    q = _rand((len(qp), hq, d), seed, dtype)
+    k = _rand((len(kp), hkv, d), seed + 1, dtype)
+    v = _rand((len(kp), hkv, d), seed + 2, dtype)
+    dout = np.random.default_rng(seed + 3).standard_normal((len(qp), hq, d))
+    return q, k, v, dout, (qp, kp, qs), (bq, bk, bqs), causal
+
+
+def pin_grad_brute_force(orc, tol=1e-12):
+    for case_i, case in enumerate(GRAD_CASES):
+        q, k, v, dout, (qp, kp, qs), (bq, bk, bqs), causal = _grad_case(orc, case_i, case)
+        dq, dk, dv, _ = orc.attention_grad(q, k, v, dout, qp, kp, qs, causal)
+        bdq, bdk, bdv = brute.grad_fd(q, k, v, dout, bq, bk, bqs, causal)
+        for name, got, ref in (("dq", dq, bdq), ("dk", dk, bdk), ("dv", dv, bdv)):
+            a, b, c = got.shape
+            for x, y, z in itertools.product(range(a), range(b), range(c)):
+                assert abs(float(ref[x][y][z]) - got[x, y, z]) <= tol, \
+                    "case %d: %s[%d,%d,%d] %r vs brute %s" % (case_i, name, x, y, z, got[x, y, z], ref[x][y][z])
+
+
+# ---------------------------------------------------------------------------
+# 8. gradient invariants and closed forms
+
+
+def pin_grad_invariants(orc):
+    rng = np.random.default_rng(91)
+    lq, lk, hq, hkv, d = 24, 40, 4, 2, 8
+    qp = np.sort(rng.choice(np.arange(10, 60), lq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(np.arange(0, 60), lk, replace=False)).astype(np.int32)
+    # values on a 1/64 grid, so that shifting every key by a grid vector is exact in float32
+    q = (rng.integers(-64, 65, (lq, hq, d)) / 64.0).astype(np.float32)
+    k = (rng.integers(-64, 65, (lk, hkv, d)) / 64.0).astype(np.float32)
+    v = (rng.integers(-64, 65, (lk, hkv, d)) / 64.0).astype(np.float32)
+    dout = rng.standard_normal((lq, hq, d))
+    dq, dk, dv, delta = orc.attention_grad(q, k, v, dout, qp, kp, None, True)
+    o, _, cnt = orc.attention(q, k, v, qp, kp, None, True)
+    group = hq // hkv
+    seen = (cnt.reshape(lq, hq) > 0)
+    for g in range(hkv):
+        # each row's dS sums to zero over its keys, so the key gradients of a KV head sum to zero
+        assert np.abs(dk[:, g].sum(0)).max() <= 1e-12 * max(1.0, np.abs(dk).max()), "sum_j dK_j != 0"
+        # each row's weights sum to one, so the value gradients sum to the rows' output gradients
+        rows_dout = (dout[:, g * group:(g + 1) * group] * seen[:, g * group:(g + 1) * group, None]).sum((0, 1))
+        assert np.abs(dv[:, g].sum(0) - rows_dout).max() <= 1e-12 * max(1.0, np.abs(rows_dout).max()), \
+            "sum_j dV_j != sum_i dO_i"
+    # D = <dO, O>
+    assert np.abs(delta - (dout * o.reshape(lq, hq, d)).sum(-1)).max() <= 1e-12
+    # shifting every key by one vector shifts each row's scores by a constant: no gradient changes
+    c = (rng.integers(-32, 33, d) / 64.0).astype(np.float32)
+    dq2, dk2, dv2, _ = orc.attention_grad(q, k + c, v, dout, qp, kp, None, True)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert np.abs(a - b).max() <= 1e-11 * max(1.0, np.abs(a).max()), "key shift changed a gradient"
+    # GQA = the KV heads repeated for every query head, key gradients summed over the group
+    kr, vr = np.repeat(k, group, axis=1), np.repeat(v, group, axis=1)
+    dq3, dk3, dv3, _ = orc.attention_grad(q, kr, vr, dout, qp, kp, None, True)
+    assert np.abs(dq3 - dq).max() <= 1e-12
+    assert np.abs(dk3.reshape(lk, hkv, group, d).sum(2) - dk).max() <= 1e-12
+    assert np.abs(dv3.reshape(lk, hkv, group, d).sum(2) - dv).max() <= 1e-12
+    # (row, head) list = the same rows of the full result
+    rows = np.array([0, 5, 23, 11], np.int64)
+    heads = np.array([3, 0, 1, 2], np.int32)
+    dqs, _, _, ds = orc.attention_grad(q, k, v, dout, qp, kp, None, True, rows=rows, heads=heads)
+    assert np.array_equal(dqs, dq[rows, heads]) and np.array_equal(ds, delta[rows, heads])
+
+
+def pin_grad_closed_forms(orc):
+    rng = np.random.default_rng(92)
+    # every row sees exactly one key (documents of length one): O_i = v_i, so dV_i = dO_i and
+    # the softmax has no freedom: dQ = dK = 0
+    n, hq, hkv, d = 6, 2, 1, 4
+    pos = np.arange(n, dtype=np.int32)
+    q = rng.standard_normal((n, hq, d)).astype(np.float32)
+    k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    dout = rng.standard_normal((n, hq, d))
+    dq, dk, dv, delta = orc.attention_grad(q, k, v, dout, pos, pos, pos, True)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    assert np.abs(dv[:, 0] - dout.sum(1)).max() <= 1e-14
+    assert np.abs(delta - (dout * v.astype(np.float64)).sum(-1)).max() <= 1e-13
+    # Q = 0: uniform weights 1/n_i over the n_i visible keys, so
+    # dV_j = sum over rows i seeing j of dO_i / n_i, dK = 0, and
+    # dQ_i = scale / n_i * sum_j <dO_i, v_j - mean_i(v)> k_j
+    lq, lk, d = 5, 7, 3
+    qp = np.array([1, 2, 4, 5, 6], np.int32)
+    kp = np.arange(lk, dtype=np.int32)
+    q = np.zeros((lq, 1, d), np.float32)
+    k = rng.standard_normal((lk, 1, d)).astype(np.float32)
+    v = rng.standard_normal((lk, 1, d)).astype(np.float32)
+    dout = rng.standard_normal((lq, 1, d))
+    scale = 0.7
+    dq, dk, dv, _ = orc.attention_grad(q, k, v, dout, qp, kp, None, True, scale=scale)
+    kk, vv = k[:, 0].astype(np.float64), v[:, 0].astype(np.float64)
+    dv_ref = np.zeros((lk, d))
+    for i in range(lq):
+        vis = kp <= qp[i]
+        ni = vis.sum()
+        dv_ref[vis] += dout[i, 0] / ni
+        vbar = vv[vis].mean(0)
+        dq_ref = scale / ni * ((vv[vis] - vbar) @ dout[i, 0]) @ kk[vis]
+        assert np.abs(dq[i, 0] - dq_ref).max() <= 1e-13, "uniform-weight dQ row %d" % i
+    assert np.all(dk == 0.0)
+    assert np.abs(dv[:, 0] - dv_ref).max() <= 1e-13
+
+
 ALL_PINS = [pin_brute_force, pin_rows_sum_to_one, pin_merge_order, pin_global_softmax, pin_merge_special,
-            pin_closed_forms, pin_gqa_and_head_split, pin_index_maps]
+            pin_closed_forms, pin_gqa_and_head_split, pin_index_maps, pin_grad_invariants, pin_grad_closed_forms,
+            pin_grad_brute_force]
