@@ -98,6 +98,10 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="instead of the headline line, time the step as ONE cpattn_partial_multi call over all "
                          "blocks (state kept in registers between blocks); one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the headline line, time the gradient step on the workload: D = <dO, O> "
+                         "once, then the backward of every KV block in arrival order (dQ summed over blocks, "
+                         "dK and dV per block); one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -138,6 +142,9 @@ def main():
         return
     if args.fused:
         fused_step(wl, share, order, step_flops, args.steps, args.warmup)
+        return
+    if args.backward:
+        backward_step(wl, share, order, step_flops, args.steps, args.warmup)
         return
 
     for _ in range(args.warmup):
@@ -235,6 +242,51 @@ def fused_step(wl, share, order, step_flops, steps, warmup):
     print(json.dumps({"metric": METRIC + ", one multi-block call per step", "value": round(tflops, 2),
                       "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
                       "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
+                      "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
+
+
+def backward_step(wl, share, order, step_flops, steps, warmup):
+    """The gradient step of the share, timed: one cpattn_bwd_delta call, then
+    one cpattn_partial_bwd call per block (its key kernel and query kernel).
+    Algorithmic work is five matrix products per visible pair (S, dP, dV, dK,
+    dQ: 2.5 times the forward's two); the kernels run seven (S and dP are
+    formed in both kernels). Prints one JSON line."""
+    import torch
+    from context_long_sequence_amd.share import bits_to_device
+    from context_long_sequence_amd import cpattn_bwd_delta, cpattn_partial_bwd
+    share.step(order)
+    dout = bits_to_device(wl.dout())
+    for _ in range(max(1, warmup)):   # (the first call also allocates the gradient buffers)
+        share.backward(dout, order)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n_launch = steps * len(order)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    n = 0
+    for _ in range(steps):
+        cpattn_bwd_delta(share.o, dout, share.delta)
+        for i, b in enumerate(order):
+            ev[2 * n].record(stream)
+            cpattn_partial_bwd(share.q, share.k_blocks[b], share.v_blocks[b], dout, share.q_pos,
+                               share.k_pos_blocks[b], share.lse, share.delta, share.dq, share.dk[b], share.dv[b],
+                               causal=share.causal, accumulate_dq=i > 0, cu_seqlens=share.cu_seqlens)
+            ev[2 * n + 1].record(stream)
+            n += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    call_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_launch)]))
+    bwd_flops = 2.5 * step_flops
+    tflops = bwd_flops / (ms * 1e-3) / 1e12
+    log("backward step: %.3f ms/step, %.1f TFLOP/s algorithmic (%.1f executed), %.3f ms per block call" %
+        (ms, tflops, tflops * 1.4, call_ms))
+    print(json.dumps({"metric": "causal-effective backward TFLOP/s of one rank share (bf16 MFMA, fp32 gradients)",
+                      "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
+                      "warmup": warmup, "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
+                      "algorithmic_flop_per_step": bwd_flops, "executed_flop_per_step": 1.4 * bwd_flops,
+                      "mean_block_call_ms": round(call_ms, 5),
                       "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
 
 

@@ -13,6 +13,9 @@ Functions (same names as the C ABI):
   cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,
                        accumulate=False, cu_seqlens=None)
   cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
+  cpattn_bwd_delta(o, dout, delta)
+  cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, causal=True, softmax_scale=0.0,
+                     accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None)
 
 Layouts: q, o [lq, hq, d]; k, v [lk, hkv, d]; lse [hq, lq] float32; positions
 int32 ascending. See include/cpattn.h for the full contract.
@@ -69,6 +72,11 @@ def load_library(path=LIB_PATH):
     lib.cpattn_partial_multi.restype = ctypes.c_int
     lib.cpattn_partial_multi.argtypes = [vp, vp, vp, ctypes.c_int, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32,
                                          i32, f32, vp, ctypes.c_int, vp, i32, vp]
+    lib.cpattn_bwd_delta.restype = ctypes.c_int
+    lib.cpattn_bwd_delta.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, i32, vp, vp]
+    lib.cpattn_partial_bwd.restype = ctypes.c_int
+    lib.cpattn_partial_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32,
+                                       f32, vp, vp, vp, i32, vp, vp, i32, vp]
     lib.cpattn_merge_lse.restype = ctypes.c_int
     lib.cpattn_merge_lse.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp]
     if path == LIB_PATH:
@@ -221,6 +229,52 @@ def cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part, stream=None):
     _check(lib, st)
 
 
+def cpattn_bwd_delta(o, dout, delta, stream=None):
+    """delta[h, i] = <dout[i, h], o[i, h]> (float32), for the backward calls."""
+    import torch
+    lib = load_library()
+    if o.dim() != 3 or tuple(dout.shape) != tuple(o.shape):
+        raise CpattnError(2, "o and dout must both be [lq, hq, d]")
+    lq, hq, d = o.shape
+    if tuple(delta.shape) != (hq, lq):
+        raise CpattnError(2, "delta must be [hq, lq]")
+    st = lib.cpattn_bwd_delta(_dev(o, "o"), _dtype_code(o), _dev(dout, "dout"), _dtype_code(dout), lq, hq, d,
+                              _dev(delta, "delta", torch.float32), _stream(stream))
+    _check(lib, st)
+
+
+def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, causal=True, softmax_scale=0.0,
+                       accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None, stream=None):
+    """Gradients of one KV block: dq (+)= this block's share, dk, dv (+)= the block's key gradients.
+
+    q, dout [lq, hq, d] bf16; k, v [lk, hkv, d] bf16; lse, delta [hq, lq] float32 (the merged LSE of
+    the forward and cpattn_bwd_delta's output); dq [lq, hq, d], dk, dv [lk, hkv, d] float32.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise CpattnError(2, "q, dout must be [lq, hq, d] and k, v [lk, hkv, d]")
+    lq, hq, d = q.shape
+    lk, hkv, d2 = k.shape
+    if d2 != d:
+        raise CpattnError(2, "q and k head dims differ")
+    if tuple(lse.shape) != (hq, lq) or tuple(delta.shape) != (hq, lq):
+        raise CpattnError(2, "lse and delta must be [hq, lq]")
+    if tuple(dq.shape) != (lq, hq, d) or tuple(dk.shape) != (lk, hkv, d) or tuple(dv.shape) != (lk, hkv, d):
+        raise CpattnError(2, "dq must be [lq, hq, d] and dk, dv [lk, hkv, d]")
+    if dout.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise CpattnError(3, "q, k, v and dout must share one dtype")
+    st = lib.cpattn_partial_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dtype_code(q), lq, lk,
+                                hq, hkv, d, _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
+                                int(bool(causal)), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                                0 if cu_seqlens is None else cu_seqlens.numel() - 1, float(softmax_scale),
+                                _dev(lse, "lse", torch.float32), _dev(delta, "delta", torch.float32),
+                                _dev(dq, "dq", torch.float32), int(bool(accumulate_dq)),
+                                _dev(dk, "dk", torch.float32), _dev(dv, "dv", torch.float32),
+                                int(bool(accumulate_dkv)), _stream(stream))
+    _check(lib, st)
+
+
 __all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_partial_multi",
-           "cpattn_merge_lse", "cpattn_version",
+           "cpattn_merge_lse", "cpattn_bwd_delta", "cpattn_partial_bwd", "cpattn_version",
            "CpattnError", "load_library", "header_functions"]

@@ -276,6 +276,95 @@ cpattn_status cpattn_partial_multi(const void* q, const void* const* k_blocks, c
                                lse, accumulate, stream);
 }
 
+cpattn_status cpattn_bwd_delta(const void* o, cpattn_dtype o_dtype, const void* dout, cpattn_dtype dout_dtype,
+                               int64_t lq, int32_t hq, int32_t head_dim, float* delta, void* stream) {
+  if (lq != 0 && (!o || !dout || !delta)) return fail(CPATTN_ERR_NULL, "o, dout and delta must be non-NULL");
+  if ((o_dtype != CPATTN_BF16 && o_dtype != CPATTN_F32) || (dout_dtype != CPATTN_BF16 && dout_dtype != CPATTN_F32))
+    return fail(CPATTN_ERR_DTYPE, "o_dtype and dout_dtype must be bf16 or float32");
+  if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
+  if (lq < 0 || hq < 1) return fail(CPATTN_ERR_SHAPE, "lq must be >= 0 and hq >= 1");
+  if (lq >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq must be < 2^31");
+  if (!aligned(o, 16) || !aligned(dout, 16)) return fail(CPATTN_ERR_ALIGN, "o and dout must be 16-byte aligned");
+  if (!aligned(delta, 4)) return fail(CPATTN_ERR_ALIGN, "delta must be 4-byte aligned");
+  const size_t nd = (size_t)lq * hq * sizeof(float);
+  if (overlaps(delta, nd, o, (size_t)lq * hq * head_dim * dsize(o_dtype)) ||
+      overlaps(delta, nd, dout, (size_t)lq * hq * head_dim * dsize(dout_dtype)))
+    return fail(CPATTN_ERR_ALIAS, "delta must not overlap o or dout");
+  if (lq == 0) return ok();
+  hipError_t e = cpattn::launch_bwd_delta(o, o_dtype == CPATTN_BF16, dout, dout_dtype == CPATTN_BF16, lq, hq,
+                                          head_dim, delta, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, const void* dout, cpattn_dtype in_dtype,
+                                 int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 const int32_t* q_pos, const int32_t* k_pos, int32_t causal,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, float softmax_scale, const float* lse,
+                                 const float* delta, float* dq, int32_t accumulate_dq, float* dk, float* dv,
+                                 int32_t accumulate_dkv, void* stream) {
+  if (lq != 0 && (!q || !dout || !lse || !delta || !dq))
+    return fail(CPATTN_ERR_NULL, "q, dout, lse, delta and dq must be non-NULL");
+  if (lk != 0 && (!k || !v || !dk || !dv)) return fail(CPATTN_ERR_NULL, "k, v, dk and dv must be non-NULL");
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_RANGE, "causal must be 0 or 1, got %d", causal);
+  if ((accumulate_dq != 0 && accumulate_dq != 1) || (accumulate_dkv != 0 && accumulate_dkv != 1))
+    return fail(CPATTN_ERR_RANGE, "accumulate_dq and accumulate_dkv must be 0 or 1");
+  if (causal && ((lq != 0 && !q_pos) || (lk != 0 && !k_pos)))
+    return fail(CPATTN_ERR_NULL, "q_pos and k_pos are required when causal");
+  if (cu_seqlens) {
+    if (causal != 1) return fail(CPATTN_ERR_RANGE, "documents (cu_seqlens) need causal = 1");
+    if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+    if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  }
+  if (in_dtype != CPATTN_BF16) return fail(CPATTN_ERR_DTYPE, "the backward takes bf16 q, k, v and dout");
+  if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
+  if (hq < 1 || hkv < 1) return fail(CPATTN_ERR_SHAPE, "hq and hkv must be >= 1 (hq=%d hkv=%d)", hq, hkv);
+  if (hq % hkv) return fail(CPATTN_ERR_SHAPE, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
+  if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
+  // a 32-row tile of one head is addressed with 32-bit buffer offsets
+  if ((int64_t)hq * head_dim * 2 * 32 >= (int64_t)1 << 31)
+    return fail(CPATTN_ERR_SHAPE, "hq * head_dim too large (a 32-row tile must span < 2 GiB)");
+  if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(CPATTN_ERR_ALIGN, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(delta, 4) || (q_pos && !aligned(q_pos, 4)) || (k_pos && !aligned(k_pos, 4)))
+    return fail(CPATTN_ERR_ALIGN, "lse, delta and positions must be 4-byte aligned");
+  const size_t nq = (size_t)lq * hq * head_dim * 2, nk = (size_t)lk * hkv * head_dim * 2;
+  const size_t ndq = (size_t)lq * hq * head_dim * 4, ndk = (size_t)lk * hkv * head_dim * 4;
+  const size_t nl = (size_t)lq * hq * sizeof(float);
+  const void* ins[] = {q, k, v, dout, lse, delta};
+  const size_t nin[] = {nq, nk, nk, nq, nl, nl};
+  void* outs[] = {dq, dk, dv};
+  const size_t nout[] = {ndq, ndk, ndk};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], nout[a], ins[b], nin[b]))
+        return fail(CPATTN_ERR_ALIAS, "dq, dk and dv must not overlap the inputs");
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], nout[a], outs[b], nout[b])) return fail(CPATTN_ERR_ALIAS, "dq, dk and dv must not overlap");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_env() && causal) {
+    cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
+    if (st == CPATTN_OK) st = check_sorted_device(k_pos, lk, "k_pos", s);
+    if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
+    if (st != CPATTN_OK) return st;
+  }
+  cpattn::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.dout = dout; p.lse = lse; p.delta = delta;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.q_pos = q_pos; p.k_pos = k_pos; p.cu_seqlens = cu_seqlens; p.n_seqs = cu_seqlens ? n_seqs : 0;
+  p.lq = (int32_t)lq; p.lk = (int32_t)lk; p.hq = hq; p.hkv = hkv;
+  p.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.causal = causal; p.acc_dq = accumulate_dq; p.acc_dkv = accumulate_dkv;
+  hipError_t e = cpattn::launch_bwd(p, head_dim, cu_seqlens != nullptr, s);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 cpattn_status cpattn_merge_lse(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
                                cpattn_dtype o_dtype, int64_t lq, int32_t hq, int32_t head_dim, void* stream) {
   if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(CPATTN_ERR_NULL, "all four buffers must be non-NULL");

@@ -1,0 +1,534 @@
+// partial_bwd.hip — gradients of one KV block's part of a context-parallel
+// rank's attention, for gfx950 (MI355X).
+//
+// Method: training with context parallelism runs the backward pass over the
+// same KV blocks as the forward (PCP page "大模型长序列显存优化：PCP与DCP序列并行
+// 实战指南", §2.3), with the same global-position masks (§3.5; zig-zag page
+// "大模型长上下文训练的挑战与突破", §4.2) and the same GQA head sharing (Halo page
+// "长上下文训练 256k 不难", Ulysses section). The pages give no formulas for it;
+// these are the gradients of the attention the forward computes. With each
+// row's FINAL log-normaliser LSE (after every block was merged) and
+// D = <dO, O>, the probabilities of a block's keys are P = exp(s - LSE), and
+//     dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// Because P uses the final LSE, the terms of one block are exactly that
+// block's share of the full gradient: dQ is the sum over blocks, and a
+// block's dK and dV are complete once every query row has been seen.
+//
+// gfx950 design (not taken from the pages, which give no kernel):
+//  * Two kernels and no atomics. The key kernel: a workgroup of four waves
+//    owns 128 keys of one KV head (32 per wave) and walks the 32-row query
+//    tiles that can see them, for every query head that reads that KV head,
+//    accumulating dK and dV in registers. The query kernel: a workgroup owns
+//    128 rows (32 per wave) of one head and walks the 32-key tiles they can
+//    see, accumulating dQ. Both recompute S and dP (seven matrix products
+//    per visible pair instead of five) in exchange for no atomic traffic
+//    and run-to-run identical results.
+//  * Each wave keeps its own side's operands in registers for the whole
+//    call (K and V of its keys, or Q and dO of its rows) and streams the
+//    other side through two LDS stages, fetched one tile ahead into
+//    registers (16-byte buffer loads; the range check zero-fills rows past
+//    the end).
+//  * Orientation, with v_mfma_f32_32x32x16_bf16: the key kernel computes
+//    S = Q K^T and dP = dO V^T, so each lane holds ONE key and 16 query rows;
+//    P and dS, rounded to bf16, are then directly the B operands of
+//    dV^T = dO^T P and dK^T = Q^T dS, whose A operands (dO^T, Q^T) are read
+//    transposed from LDS with ds_read_b64_tr_b16, and the accumulators keep
+//    each lane on its key. The query kernel is the mirror: S^T = K Q^T,
+//    dP^T = V dO^T, one query row per lane (its LSE and D are scalars of
+//    the lane), and dQ^T = K^T dS^T with K^T read transposed.
+//  * Tiles are row-major in LDS with one XOR swizzle of 16-byte chunks that
+//    keeps both the row reads (ds_read_b128, 16 rows at one chunk) and the
+//    transposed reads (4 rows x 4 chunks) free of bank conflicts.
+//  * Workgroup ids are remapped so that consecutive logical tiles run on
+//    one XCD (shared L2); the tiles with the most work go first.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "tile_io.hpp"
+
+namespace cpattn {
+
+constexpr int kBwdThreads = 256;  // four waves
+
+template <int D>
+struct BwdTile {
+  static constexpr int kRowBytes = 2 * D;              // one bf16 row
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kBytes = 32 * kRowBytes;        // a 32-row tile
+  static constexpr int kUnits = kBytes / 16 / kBwdThreads;  // 16-byte loads per thread per tile
+  static constexpr int kNQ = D / 16;                   // k-steps over the head dimension
+  static constexpr int kNDT = D / 32;                  // 32-column blocks of the head dimension
+  // chunk ^ swz(row): 16 consecutive rows at one chunk hit 16 distinct
+  // 16-byte bank groups, and so do 4 consecutive rows x 4 consecutive chunks
+  static constexpr int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  static constexpr int off(int row, int chunk) { return row * kRowBytes + ((chunk ^ swz(row)) << 4); }
+};
+
+// 32 rows of one head of a [n_rows][heads][D] bf16 tensor into registers:
+// thread t holds 16-byte units t, t + 256, ... of the tile (row-major);
+// rows at or past n_rows read as zeros.
+template <int D>
+__device__ __forceinline__ void fetch_rows(u32x4_t* regs, const char* head_base, int row_stride, int r0, int n_rows,
+                                           int tid) {
+  using T = BwdTile<D>;
+  const int rows = clamp_rows(n_rows - r0, 32);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head_base + (int64_t)r0 * row_stride, (int64_t)rows * row_stride);
+#pragma unroll
+  for (int u = 0; u < T::kUnits; ++u) {
+    const int unit = tid + kBwdThreads * u;
+    regs[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (unit / T::kChunks) * row_stride + (unit % T::kChunks) * 16,
+                                                    0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void commit_rows(char CPATTN_LDS* tile, const u32x4_t* regs, int tid) {
+  using T = BwdTile<D>;
+#pragma unroll
+  for (int u = 0; u < T::kUnits; ++u) {
+    const int unit = tid + kBwdThreads * u;
+    *(u32x4_t CPATTN_LDS*)(tile + T::off(unit / T::kChunks, unit % T::kChunks)) = regs[u];
+  }
+}
+
+// Transposed operand: for a tile whose rows are the contraction index
+// (32 of them) and whose columns are the output rows, the A operand of k-step
+// hf (rows 16hf .. 16hf+15) and column block dt. The contraction order matches
+// the accumulator layout of the B side: lane half g holds rows 16hf + 4g + 0..3
+// and 16hf + 8 + 4g + 0..3. a0/a8 are the lane's byte offsets in rows 0..15
+// and 8..23 (the swizzle differs between them).
+__device__ __forceinline__ bf16x8_t read_tr(const char CPATTN_LDS* tile, int a0, int a8, int hf, int row_bytes) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t CPATTN_LDS*)(tile + a0 + 16 * hf * row_bytes));
+  const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t CPATTN_LDS*)(tile + a8 + 16 * hf * row_bytes));
+  return __builtin_bit_cast(bf16x8_t, (i16x8)__builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// this lane's transposed-read offsets (see read_tr) for column block dt
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int dt, int& a0, int& a8) {
+  using T = BwdTile<D>;
+  const int g = lane >> 5;
+  const int vr = 4 * g + ((lane & 15) >> 2);              // row within a 16-row group
+  const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  a0 = T::off(vr, col >> 3) + ((col & 7) << 1);
+  a8 = T::off(vr + 8, col >> 3) + ((col & 7) << 1);
+}
+
+// End of the document holding position x: the first offset > x (INT32_MAX
+// past the last one).
+__device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_seqs, int32_t x) {
+  const int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, x);
+  return idx <= n_seqs ? cu_seqlens[idx] : 0x7FFFFFFF;
+}
+
+// ---------------------------------------------------------------------------
+// Key kernel: dK and dV of 128 keys of one KV head.
+
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
+  __shared__ __attribute__((aligned(1024))) char q_s0[TB], q_s1[TB], o_s0[TB], o_s1[TB];
+  __shared__ __attribute__((aligned(16))) float l_s0[32], l_s1[32], d_s0[32], d_s1[32];
+  __shared__ __attribute__((aligned(16))) int32_t p_s0[32], p_s1[32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int hk = L / p.n_tiles;
+  const int kt = L % p.n_tiles;  // early keys (seen by the most rows) first
+  const int G = p.hq / p.hkv;
+  const int lq = p.lq, lk = p.lk;
+  const int wg_j0 = kt * 128, wg_j1 = min(wg_j0 + 128, lk);
+  const int j0 = wg_j0 + 32 * wave;
+  const int kj = min(j0 + li, lk - 1);              // this lane's key (clamped)
+  const bool key_valid = j0 + li < lk;
+
+  // the wave's keys: B operands of S = Q K^T and dP = dO V^T
+  bf16x8_t kreg[NQ], vreg[NQ];
+  {
+    const int64_t off = ((int64_t)kj * p.hkv + hk) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) {
+      kreg[ks] = *(const bf16x8_t*)((const __bf16*)p.k + off + 16 * ks);
+      vreg[ks] = *(const bf16x8_t*)((const __bf16*)p.v + off + 16 * ks);
+    }
+  }
+  // rows that see key j: q_pos >= k_pos[j] and, with documents, q_pos < end of k's document
+  const int32_t my_kpos = p.causal ? p.k_pos[kj] : 0;
+  const int32_t my_kend = VARLEN ? doc_end(p.cu_seqlens, p.n_seqs, my_kpos) : 0;
+  int i_lo = 0, i_hi = lq;
+  if (p.causal) {
+    i_lo = wave_upper_bound(p.q_pos, lq, p.k_pos[wg_j0] - 1);
+    if constexpr (VARLEN) i_hi = wave_upper_bound(p.q_pos, lq, doc_end(p.cu_seqlens, p.n_seqs, p.k_pos[wg_j1 - 1]) - 1);
+  }
+  const int nqt = i_hi > i_lo ? (i_hi - i_lo + 31) / 32 : 0;
+  const int n_it = G * nqt;
+
+  // ---- query tiles: (head, 32 rows) per iteration, head-major ----
+  const int q_stride = p.hq * D * 2;
+  u32x4_t qr[T::kUnits], orr[T::kUnits];
+  float lr = 0.f, dr = 0.f;
+  int32_t pr = 0;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int hh = hk * G + it / nqt;
+    const int i0 = i_lo + 32 * (it % nqt);
+    fetch_rows<D>(qr, (const char*)p.q + (int64_t)hh * D * 2, q_stride, i0, lq, tid);
+    fetch_rows<D>(orr, (const char*)p.dout + (int64_t)hh * D * 2, q_stride, i0, lq, tid);
+    if (tid < 32) {
+      const int i = i0 + tid;
+      const bool ok = i < lq;
+      const float l = ok ? p.lse[(int64_t)hh * lq + i] : neg_inf();
+      lr = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // rows past the end, or that see nothing: P = 0
+      dr = ok ? p.delta[(int64_t)hh * lq + i] : 0.f;
+      pr = (ok && p.causal) ? p.q_pos[i] : (int32_t)0x80000000;
+    }
+  };
+  auto commit = [&](int st) __attribute__((always_inline)) {
+    commit_rows<D>(st ? (char CPATTN_LDS*)q_s1 : (char CPATTN_LDS*)q_s0, qr, tid);
+    commit_rows<D>(st ? (char CPATTN_LDS*)o_s1 : (char CPATTN_LDS*)o_s0, orr, tid);
+    if (tid < 32) {
+      (st ? l_s1 : l_s0)[tid] = lr;
+      (st ? d_s1 : d_s0)[tid] = dr;
+      (st ? p_s1 : p_s0)[tid] = pr;
+    }
+  };
+
+  int ra[NQ];         // row reads: row li, chunk 2ks + g
+#pragma unroll
+  for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
+  int ta0[NDT], ta8[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) tr_offsets<D>(lane, dt, ta0[dt], ta8[dt]);
+
+  f32x16_t dk_acc[NDT], dv_acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk_acc[dt] = f32x16_t{};
+    dv_acc[dt] = f32x16_t{};
+  }
+
+  if (n_it > 0) {
+    fetch(0);
+    commit(0);
+  }
+  phase_barrier();
+  for (int it = 0; it < n_it; ++it) {
+    const int st = it & 1;
+    if (it + 1 < n_it) fetch(it + 1);
+    const char CPATTN_LDS* ql = st ? (const char CPATTN_LDS*)q_s1 : (const char CPATTN_LDS*)q_s0;
+    const char CPATTN_LDS* ol = st ? (const char CPATTN_LDS*)o_s1 : (const char CPATTN_LDS*)o_s0;
+    const float CPATTN_LDS* ll = st ? (const float CPATTN_LDS*)l_s1 : (const float CPATTN_LDS*)l_s0;
+    const float CPATTN_LDS* dl = st ? (const float CPATTN_LDS*)d_s1 : (const float CPATTN_LDS*)d_s0;
+    const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
+
+    // S = Q K^T, dP = dO V^T (rows: the tile's queries; column: this lane's key)
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(ql + ra[ks]), kreg[ks], s, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(ol + ra[ks]), vreg[ks], dp, 0, 0, 0);
+
+    // P = exp(s - LSE) on visible pairs, dS = P (dP - D); register r is query row 8(r/4) + 4g + r%4
+    uint32_t pp[8], pd[8];
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 l4 = *(const f32x4 CPATTN_LDS*)(ll + 8 * rr + 4 * g);
+      const f32x4 d4 = *(const f32x4 CPATTN_LDS*)(dl + 8 * rr + 4 * g);
+      i32x4 q4 = {0, 0, 0, 0};
+      if (p.causal) q4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
+      float pv[4], dv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bool vis = key_valid;
+        if (p.causal) {
+          vis = vis & (q4[c] >= my_kpos);
+          if (VARLEN) vis = vis & (q4[c] < my_kend);
+        }
+        pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
+        dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+      }
+      pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
+      pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
+      pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+      pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+    }
+
+    // dV^T += dO^T P, dK^T += Q^T dS
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const u32x4 bp = {pp[4 * hf], pp[4 * hf + 1], pp[4 * hf + 2], pp[4 * hf + 3]};
+      const u32x4 bd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ol, ta0[dt], ta8[dt], hf, T::kRowBytes),
+                                                             __builtin_bit_cast(bf16x8_t, bp), dv_acc[dt], 0, 0, 0);
+        dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ql, ta0[dt], ta8[dt], hf, T::kRowBytes),
+                                                             __builtin_bit_cast(bf16x8_t, bd), dk_acc[dt], 0, 0, 0);
+      }
+    }
+    if (it + 1 < n_it) commit(st ^ 1);
+    phase_barrier();
+  }
+
+  // ---- store: lane li holds key j0 + li, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
+  if (!key_valid) return;
+  float* dkrow = p.dk + ((int64_t)kj * p.hkv + hk) * D;
+  float* dvrow = p.dv + ((int64_t)kj * p.hkv + hk) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d0 = 32 * dt + 8 * rr + 4 * g;
+      float4 a = make_float4(dk_acc[dt][4 * rr] * p.scale, dk_acc[dt][4 * rr + 1] * p.scale,
+                             dk_acc[dt][4 * rr + 2] * p.scale, dk_acc[dt][4 * rr + 3] * p.scale);
+      float4 b = make_float4(dv_acc[dt][4 * rr], dv_acc[dt][4 * rr + 1], dv_acc[dt][4 * rr + 2], dv_acc[dt][4 * rr + 3]);
+      if (p.acc_dkv) {
+        const float4 oa = *(const float4*)(dkrow + d0), ob = *(const float4*)(dvrow + d0);
+        a.x += oa.x; a.y += oa.y; a.z += oa.z; a.w += oa.w;
+        b.x += ob.x; b.y += ob.y; b.z += ob.z; b.w += ob.w;
+      }
+      *(float4*)(dkrow + d0) = a;
+      *(float4*)(dvrow + d0) = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Query kernel: dQ of 128 rows of one query head.
+
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
+  __shared__ __attribute__((aligned(1024))) char k_s0[TB], k_s1[TB], v_s0[TB], v_s1[TB];
+  __shared__ __attribute__((aligned(16))) int32_t p_s0[32], p_s1[32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int h = L / p.n_tiles;
+  const int qt = p.n_tiles - 1 - L % p.n_tiles;  // late rows (that see the most keys) first
+  const int hk = h / (p.hq / p.hkv);
+  const int lq = p.lq, lk = p.lk;
+  const int wg_r0 = qt * 128, wg_r1 = min(wg_r0 + 128, lq);
+  const int r0 = wg_r0 + 32 * wave;
+  const int qi = min(r0 + li, lq - 1);              // this lane's row (clamped)
+  const bool row_valid = r0 + li < lq;
+
+  // the wave's rows: B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8_t qreg[NQ], dreg[NQ];
+  {
+    const int64_t off = ((int64_t)qi * p.hq + h) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) {
+      qreg[ks] = *(const bf16x8_t*)((const __bf16*)p.q + off + 16 * ks);
+      dreg[ks] = *(const bf16x8_t*)((const __bf16*)p.dout + off + 16 * ks);
+    }
+  }
+  const float l_raw = p.lse[(int64_t)h * lq + qi];
+  const float lse2 = (!row_valid || l_raw == neg_inf()) ? __builtin_inff() : l_raw * kLog2e;
+  const float dlt = row_valid ? p.delta[(int64_t)h * lq + qi] : 0.f;
+  const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
+  const int32_t my_start = VARLEN ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
+
+  // keys the workgroup's rows can see
+  int kb = 0, ke = lk;
+  if (p.causal) {
+    ke = wave_upper_bound(p.k_pos, lk, p.q_pos[wg_r1 - 1]);
+    if constexpr (VARLEN) kb = wave_upper_bound(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
+  }
+  const int nt = ke > kb ? (ke - kb + 31) / 32 : 0;
+
+  const int kv_stride = p.hkv * D * 2;
+  const char* kbase = (const char*)p.k + (int64_t)hk * D * 2;
+  const char* vbase = (const char*)p.v + (int64_t)hk * D * 2;
+  u32x4_t kr[T::kUnits], vr[T::kUnits];
+  int32_t pr = 0;
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int j0 = kb + 32 * t;
+    fetch_rows<D>(kr, kbase, kv_stride, j0, lk, tid);
+    fetch_rows<D>(vr, vbase, kv_stride, j0, lk, tid);
+    if (tid < 32) pr = (p.causal && j0 + tid < lk) ? p.k_pos[j0 + tid] : 0x7FFFFFFF;
+  };
+  auto commit = [&](int st) __attribute__((always_inline)) {
+    commit_rows<D>(st ? (char CPATTN_LDS*)k_s1 : (char CPATTN_LDS*)k_s0, kr, tid);
+    commit_rows<D>(st ? (char CPATTN_LDS*)v_s1 : (char CPATTN_LDS*)v_s0, vr, tid);
+    if (tid < 32) (st ? p_s1 : p_s0)[tid] = pr;
+  };
+
+  int ra[NQ];
+#pragma unroll
+  for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
+  int ta0[NDT], ta8[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) tr_offsets<D>(lane, dt, ta0[dt], ta8[dt]);
+
+  f32x16_t acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16_t{};
+
+  if (nt > 0) {
+    fetch(0);
+    commit(0);
+  }
+  phase_barrier();
+  for (int t = 0; t < nt; ++t) {
+    const int st = t & 1;
+    if (t + 1 < nt) fetch(t + 1);
+    const char CPATTN_LDS* kl = st ? (const char CPATTN_LDS*)k_s1 : (const char CPATTN_LDS*)k_s0;
+    const char CPATTN_LDS* vl = st ? (const char CPATTN_LDS*)v_s1 : (const char CPATTN_LDS*)v_s0;
+    const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
+
+    // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query row)
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(kl + ra[ks]), qreg[ks], s, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(vl + ra[ks]), dreg[ks], dp, 0, 0, 0);
+
+    // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile
+    const int lim = min(lk - (kb + 32 * t), 32);
+    uint32_t pd[8];
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      i32x4 k4 = {0, 0, 0, 0};
+      if (p.causal) k4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
+      float dv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bool vis = 8 * rr + 4 * g + c < lim;
+        if (p.causal) {
+          vis = vis & (k4[c] <= my_qpos);
+          if (VARLEN) vis = vis & (k4[c] >= my_start);
+        }
+        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -lse2)) : 0.f;
+        dv[c] = pv * (dp[4 * rr + c] - dlt);
+      }
+      pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+      pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+    }
+
+    // dQ^T += K^T dS^T
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const u32x4 bd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kl, ta0[dt], ta8[dt], hf, T::kRowBytes),
+                                                          __builtin_bit_cast(bf16x8_t, bd), acc[dt], 0, 0, 0);
+    }
+    if (t + 1 < nt) commit(st ^ 1);
+    phase_barrier();
+  }
+
+  // ---- store: lane holds row qi, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
+  if (!row_valid) return;
+  float* dqrow = p.dq + ((int64_t)qi * p.hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d0 = 32 * dt + 8 * rr + 4 * g;
+      float4 a = make_float4(acc[dt][4 * rr] * p.scale, acc[dt][4 * rr + 1] * p.scale, acc[dt][4 * rr + 2] * p.scale,
+                             acc[dt][4 * rr + 3] * p.scale);
+      if (p.acc_dq) {
+        const float4 o = *(const float4*)(dqrow + d0);
+        a.x += o.x; a.y += o.y; a.z += o.z; a.w += o.w;
+      }
+      *(float4*)(dqrow + d0) = a;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// D = <dO, O> per (row, head): D/8 lanes per pair, 8 elements each.
+
+template <typename TO, typename TD, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const void* o, const void* dout, float* delta, int64_t lq,
+                                                        int32_t hq) {
+  constexpr int LPP = D / 8;
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPP;
+  const int sub = threadIdx.x % LPP;
+  const int64_t n = lq * hq;
+  float acc = 0.f;
+  if (pair < n) {
+    const int64_t base = pair * D + 8 * sub;
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (sizeof(TO) == 2) a[e] = (float)((const __bf16*)o)[base + e];
+      else a[e] = ((const float*)o)[base + e];
+      if constexpr (sizeof(TD) == 2) b[e] = (float)((const __bf16*)dout)[base + e];
+      else b[e] = ((const float*)dout)[base + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(a[e], b[e], acc);
+  }
+#pragma unroll
+  for (int m = LPP / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (pair < n && sub == 0) delta[(pair % hq) * lq + pair / hq] = acc;
+}
+
+// ---------------------------------------------------------------------------
+
+template <int D, bool VARLEN>
+static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {
+  if (p.lk > 0) {
+    BwdParams a = p;
+    a.n_tiles = (p.lk + 127) / 128;
+    a.n_wg = a.n_tiles * p.hkv;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.lq > 0) {
+    BwdParams a = p;
+    a.n_tiles = (p.lq + 127) / 128;
+    a.n_wg = a.n_tiles * p.hq;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream) {
+  if (head_dim == 128) return varlen ? launch_bwd_typed<128, true>(p, stream) : launch_bwd_typed<128, false>(p, stream);
+  return varlen ? launch_bwd_typed<64, true>(p, stream) : launch_bwd_typed<64, false>(p, stream);
+}
+
+template <int D>
+static hipError_t launch_delta_d(const void* o, int o_bf16, const void* dout, int do_bf16, int64_t lq, int32_t hq,
+                                 float* delta, hipStream_t stream) {
+  const int64_t threads = lq * hq * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (o_bf16 && do_bf16) hipLaunchKernelGGL((bwd_delta_kernel<__bf16, __bf16, D>), grid, block, 0, stream, o, dout, delta, lq, hq);
+  else if (o_bf16) hipLaunchKernelGGL((bwd_delta_kernel<__bf16, float, D>), grid, block, 0, stream, o, dout, delta, lq, hq);
+  else if (do_bf16) hipLaunchKernelGGL((bwd_delta_kernel<float, __bf16, D>), grid, block, 0, stream, o, dout, delta, lq, hq);
+  else hipLaunchKernelGGL((bwd_delta_kernel<float, float, D>), grid, block, 0, stream, o, dout, delta, lq, hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(const void* o, int o_bf16, const void* dout, int do_bf16, int64_t lq, int32_t hq,
+                            int32_t head_dim, float* delta, hipStream_t stream) {
+  if (lq * hq == 0) return hipSuccess;
+  if (head_dim == 128) return launch_delta_d<128>(o, o_bf16, dout, do_bf16, lq, hq, delta, stream);
+  return launch_delta_d<64>(o, o_bf16, dout, do_bf16, lq, hq, delta, stream);
+}
+
+}  // namespace cpattn

@@ -8,7 +8,8 @@ the C ABI. This is the loop of the FCP page ("ä»Žå›ºå®šçŽ¯åˆ°è‡ªç”±æ‹“æ‰‘ï¼šFCPå
 """
 import numpy as np
 
-from . import cpattn_merge_lse, cpattn_partial, cpattn_partial_multi, cpattn_varlen_partial, cpattn_zigzag_index
+from . import (cpattn_bwd_delta, cpattn_merge_lse, cpattn_partial, cpattn_partial_bwd, cpattn_partial_multi,
+               cpattn_varlen_partial, cpattn_zigzag_index)
 
 
 def bits_to_device(a, device="cuda"):
@@ -97,6 +98,31 @@ class RankShare:
         else:
             raise ValueError(mode)
         return self.o, self.lse
+
+
+    def backward(self, dout, order, lse=None):
+        """Gradients of the step: dq [lq, hq, d] and per-block dk, dv [lk_b, hkv, d]
+        (float32), with every block's backward run in `order`.
+
+        Uses the merged (self.o, self.lse) of the last forward step (or `lse`):
+        D = <dO, O> once, then one cpattn_partial_bwd call per block, the first
+        writing dq and the others adding to it; each block's dk, dv are written.
+        """
+        import torch
+        lq, hq, d = self.q.shape
+        dev = self.q.device
+        if getattr(self, "dq", None) is None:
+            self.dq = torch.empty((lq, hq, d), dtype=torch.float32, device=dev)
+            self.delta = torch.empty((hq, lq), dtype=torch.float32, device=dev)
+            self.dk = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in self.k_blocks]
+            self.dv = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in self.k_blocks]
+        lse = self.lse if lse is None else lse
+        cpattn_bwd_delta(self.o, dout, self.delta)
+        for i, b in enumerate(order):
+            cpattn_partial_bwd(self.q, self.k_blocks[b], self.v_blocks[b], dout, self.q_pos, self.k_pos_blocks[b],
+                               lse, self.delta, self.dq, self.dk[b], self.dv[b], causal=self.causal,
+                               accumulate_dq=i > 0, accumulate_dkv=False, cu_seqlens=self.cu_seqlens)
+        return self.dq, self.dk, self.dv
 
 
 def share_from_workload(wl, device="cuda", blocks=None):

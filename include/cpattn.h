@@ -181,6 +181,59 @@ cpattn_status cpattn_partial_multi(const void *q, const void *const *k_blocks, c
 cpattn_status cpattn_merge_lse(void *o_acc, float *lse_acc, const void *o_part, const float *lse_part,
                                cpattn_dtype o_dtype, int64_t lq, int32_t hq, int32_t head_dim, void *stream);
 
+/*
+ * D = <dO, O> of every (row, head), the one per-row quantity the gradients
+ * need besides the log-normaliser: the derivative of the softmax
+ * normalisation contributes -P·D to every score's gradient. Training with
+ * context parallelism runs the backward pass over the same KV blocks as the
+ * forward (PCP page, §2.3); D is computed once per step from the final O and
+ * its gradient, before the per-block backward calls. Device memory, enqueued
+ * on `stream`.
+ *
+ *  o      [lq][hq][head_dim], o_dtype (bf16 or float32): the merged output
+ *  dout   [lq][hq][head_dim], dout_dtype (bf16 or float32): dLoss/dO
+ *  delta  [hq][lq] float32 out, summed in float32
+ * head_dim must be 64 or 128; delta must not overlap o or dout.
+ */
+cpattn_status cpattn_bwd_delta(const void *o, cpattn_dtype o_dtype, const void *dout, cpattn_dtype dout_dtype,
+                               int64_t lq, int32_t hq, int32_t head_dim, float *delta, void *stream);
+
+/*
+ * Gradients of one KV block's part of the attention (device memory, enqueued
+ * on `stream`): the backward of cpattn_partial / cpattn_varlen_partial for
+ * one block, given the rows' FINAL log-normalisers (after every block was
+ * merged) and D from cpattn_bwd_delta. With P = exp(s - LSE) on the visible
+ * pairs and dS = P (dO·v - D):
+ *     dQ += scale · dS K   (this block's share; summed over blocks),
+ *     dK  = scale · dS^T Q,  dV = P^T dO   (complete for this block's keys
+ *                                          once every local row is seen).
+ * Query heads sharing a KV head add into its dK, dV (GQA).
+ *
+ *  q, dout  [lq][hq][head_dim] bf16;  k, v [lk][hkv][head_dim] bf16
+ *  q_pos, k_pos, causal, cu_seqlens, n_seqs   masks as in cpattn_partial
+ *                (cu_seqlens == NULL: no documents; otherwise DEVICE offsets
+ *                as in cpattn_varlen_partial, and causal must be 1)
+ *  softmax_scale <= 0 selects 1/sqrt(head_dim)
+ *  lse    [hq][lq] float32, the merged LSE of the forward (a row with -inf
+ *         sees no key and gets no gradient)
+ *  delta  [hq][lq] float32 from cpattn_bwd_delta
+ *  dq     [lq][hq][head_dim] float32; accumulate_dq 0: written, 1: added to
+ *  dk, dv [lk][hkv][head_dim] float32; accumulate_dkv 0: written, 1: added to
+ *
+ * bf16 inputs only (CPATTN_ERR_DTYPE otherwise); head_dim 64 or 128;
+ * hq % hkv == 0. Outputs must not overlap the inputs or each other. lq == 0:
+ * dk, dv get zeros (or are left as they are when accumulating); lk == 0
+ * likewise for dq. The two kernels (keys, then queries) write disjoint
+ * outputs with no atomics: results are identical from run to run.
+ */
+cpattn_status cpattn_partial_bwd(const void *q, const void *k, const void *v, const void *dout, cpattn_dtype in_dtype,
+                                 int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 const int32_t *q_pos, const int32_t *k_pos, int32_t causal,
+                                 const int32_t *cu_seqlens, int32_t n_seqs, float softmax_scale,
+                                 const float *lse, const float *delta,
+                                 float *dq, int32_t accumulate_dq, float *dk, float *dv, int32_t accumulate_dkv,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

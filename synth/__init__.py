@@ -34,7 +34,7 @@ def bf16_bits_to_f32(bits):
 # ---------------------------------------------------------------------------
 # random tensors
 
-_TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+_TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "dout": 3}
 
 
 def normal_tensor(shape, seed, which, block=0, sigma=1.0, dtype="bf16"):
@@ -129,6 +129,10 @@ class Workload:
 
     def q(self):
         return normal_tensor((self.lq, self.hq, self.d), self.seed, "q", 0, self.sigma, self.dtype)
+
+    def dout(self):
+        """Output gradient for the backward: N(0,1), shape and dtype of Q."""
+        return normal_tensor((self.lq, self.hq, self.d), self.seed, "dout", 0, 1.0, self.dtype)
 
     def kv_block(self, b, which):
         return normal_tensor((self.block_len(b), self.hkv, self.d), self.seed, which, b, self.sigma, self.dtype)

@@ -16,7 +16,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = cp.header_functions()
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
-                          "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse"}
+                          "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse", "cpattn_bwd_delta",
+                          "cpattn_partial_bwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -113,6 +114,41 @@ def test_multi_rejects(lib):
     assert call(lks=bad_lkp) == STATUS["ERR_SHAPE"]           # the second block's length
     assert call(o=B + 0x1000 + 16) == STATUS["ERR_ALIAS"]     # o overlaps the second block's k
     assert call(acc=2) == STATUS["ERR_RANGE"]
+
+
+DO, DL, DK, DV = 0x90000, 0xA0000, 0xB0000, 0xC0000
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+def test_backward_rejects(lib):
+    def bwd(q=A, dt=0, lq=8, lk=8, hq=1, hkv=1, hd=64, qp=P, kp=K, causal=1, cu=0, ns=0, scale=0.0, dq=O, adq=0,
+            dk=DK, dv=DV, adkv=0, delta=DL):
+        return lib.cpattn_partial_bwd(q, B, C, DO, dt, lq, lk, hq, hkv, hd, qp, kp, causal, cu, ns, scale, L, delta,
+                                      dq, adq, dk, dv, adkv, 0)
+    assert bwd(dq=0) == STATUS["ERR_NULL"]
+    assert bwd(dk=0) == STATUS["ERR_NULL"]
+    assert bwd(delta=0) == STATUS["ERR_NULL"]
+    assert bwd(qp=0) == STATUS["ERR_NULL"]                     # causal needs positions
+    assert bwd(dt=1) == STATUS["ERR_DTYPE"]                    # float32 inputs are not taken
+    assert bwd(hd=96) == STATUS["ERR_SHAPE"]
+    assert bwd(hq=6, hkv=4) == STATUS["ERR_SHAPE"]
+    assert bwd(lk=1 << 31) == STATUS["ERR_SHAPE"]
+    assert bwd(causal=2) == STATUS["ERR_RANGE"]
+    assert bwd(adq=2) == STATUS["ERR_RANGE"]
+    assert bwd(adkv=3) == STATUS["ERR_RANGE"]
+    assert bwd(cu=0x80000, ns=1, causal=0) == STATUS["ERR_RANGE"]   # documents need causal
+    assert bwd(cu=0x80000, ns=0) == STATUS["ERR_SHAPE"]
+    assert bwd(scale=float("nan")) == STATUS["ERR_RANGE"]
+    assert bwd(dq=O + 4) == STATUS["ERR_ALIGN"]
+    assert bwd(dv=DK + 16) == STATUS["ERR_ALIAS"]              # dk and dv overlap
+    assert bwd(dq=A + 16) == STATUS["ERR_ALIAS"]               # dq overlaps q
+    assert bwd(dk=DL) == STATUS["ERR_ALIAS"]                   # dk overlaps delta
+    # delta
+    assert lib.cpattn_bwd_delta(0, 0, DO, 0, 8, 1, 64, DL, 0) == STATUS["ERR_NULL"]
+    assert lib.cpattn_bwd_delta(O, 7, DO, 0, 8, 1, 64, DL, 0) == STATUS["ERR_DTYPE"]
+    assert lib.cpattn_bwd_delta(O, 0, DO, 0, 8, 1, 80, DL, 0) == STATUS["ERR_SHAPE"]
+    assert lib.cpattn_bwd_delta(O, 0, DO, 0, 8, 1, 64, O + 16, 0) == STATUS["ERR_ALIAS"]
+    assert lib.cpattn_bwd_delta(O, 0, DO + 8, 0, 8, 1, 64, DL, 0) == STATUS["ERR_ALIGN"]
 
 
 def test_last_error_is_thread_local(lib):

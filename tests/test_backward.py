@@ -1,0 +1,251 @@
+"""Gradients through the C ABI (cpattn_bwd_delta + cpattn_partial_bwd) against
+the fp64 oracle's gradients.
+
+Tolerance: the kernels round P and dS to bf16 (unit roundoff 2^-9) before the
+matrix products and accumulate in float32; O reaches D = <dO, O> rounded to
+bf16 by the forward. Each gradient element is a sum of terms that each carry
+a relative error of a few units of 2^-9, so the error is a small multiple of
+2^-9 times the size of the terms. The bar is max|g - g_ref| <= 1e-2 *
+max|g_ref| per tensor (five units of 2^-9 relative to the largest gradient),
+and the root-mean-square error <= 4e-3 * the root-mean-square of g_ref. A
+reference that is exactly zero by cancellation must come out below 1e-5.
+"""
+import numpy as np
+import pytest
+
+from test_gpu_parity import say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL_MAX = 1e-2
+GRAD_TOL_RMS = 4e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle.get()
+
+
+def grad_compare(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what + ": non-finite gradient"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    rms_ref = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    rms_err = float(np.sqrt(np.mean((got - ref) ** 2))) if ref.size else 0.0
+    say("%s: max err %.3e of max %.3e (%.2e), rms err %.3e of rms %.3e (%.2e)" % (
+        what, err, scale, err / scale if scale else 0.0, rms_err, rms_ref, rms_err / rms_ref if rms_ref else 0.0))
+    if scale == 0.0:
+        # a reference that is zero by cancellation (one visible key: dP = D, so
+        # dS = 0) comes out at float32 rounding level: D and dP are summed in
+        # different orders; inputs here are of unit size
+        assert err <= 1e-5, what + ": gradient must vanish"
+        return
+    assert err <= GRAD_TOL_MAX * scale, "%s: max error %.3e > %.1e * %.3e" % (what, err, GRAD_TOL_MAX, scale)
+    assert rms_err <= GRAD_TOL_RMS * rms_ref, "%s: rms error %.3e > %.1e * %.3e" % (what, rms_err, GRAD_TOL_RMS,
+                                                                                   rms_ref)
+
+
+def oracle_grads(orc, wl, rows=None, heads=None):
+    """The oracle's gradients for a workload (positions from its own closed forms,
+    keys of every block in block-id order); dk, dv split per block."""
+    docs = wl.doc_lens()
+    qp, qs = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
+    kps = []
+    for b in range(wl.n_blocks):
+        if wl.block_kind == "rank_shares":
+            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
+        elif wl.block_kind == "chunks":
+            c = wl.S // wl.n_blocks
+            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
+        else:
+            kps.append(np.arange(wl.S, dtype=np.int32))
+    k = wl.kv_all("k")
+    v = wl.kv_all("v")
+    from synth import bf16_bits_to_f32
+    dout = bf16_bits_to_f32(wl.dout()).astype(np.float64)
+    dq, dk, dv, _ = orc.attention_grad(wl.q(), k, v, dout, qp, np.concatenate(kps), qs if docs is not None else None,
+                                       True, rows=rows, heads=heads)
+    if rows is not None:
+        return dq, None, None
+    bounds = np.cumsum([0] + [len(p) for p in kps])
+    return dq, [dk[bounds[b]:bounds[b + 1]] for b in range(wl.n_blocks)], \
+        [dv[bounds[b]:bounds[b + 1]] for b in range(wl.n_blocks)]
+
+
+def _reduced():
+    from synth import WORKLOADS as W
+    return {
+        "c0b": W["c0"].scaled(name="c0b", dtype="bf16"),
+        "c1r": W["c1"].scaled(name="c1r", S=4096, hq=4, hkv=4),
+        "c2r": W["c2"].scaled(name="c2r", S=1024),
+        "c3r": W["c3"].scaled(name="c3r", S=8192, hq=2, hkv=2, docs=(256, 2048)),
+        "c4r": W["c4"].scaled(name="c4r", S=4096, hq=8, hkv=2),
+    }
+
+
+def _run(torch, wl):
+    from context_long_sequence_amd.share import bits_to_device, share_from_workload
+    share = share_from_workload(wl)
+    order = list(wl.arrival())
+    share.step(order, "accumulate")
+    dout = bits_to_device(wl.dout())
+    dq, dk, dv = share.backward(dout, order)
+    torch.cuda.synchronize()
+    return share, dout, dq, dk, dv
+
+
+@pytest.mark.parametrize("name", ["c0b", "c1r", "c2r", "c3r", "c4r"])
+def test_backward_reduced_all(torch_cuda, orc, name):
+    wl = _reduced()[name]
+    say("backward %s: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d, wl.n_blocks))
+    _, _, dq, dk, dv = _run(torch_cuda, wl)
+    rdq, rdk, rdv = oracle_grads(orc, wl)
+    grad_compare(dq.cpu().numpy(), rdq, name + " dq")
+    grad_compare(np.concatenate([x.cpu().numpy() for x in dk]), np.concatenate(rdk), name + " dk")
+    grad_compare(np.concatenate([x.cpu().numpy() for x in dv]), np.concatenate(rdv), name + " dv")
+
+
+def test_backward_full_size_c1_sampled(torch_cuda, orc):
+    """The 64K-token zig-zag cp8 rank share at full size, in the launch
+    configuration the benchmark times: dq on sampled rows against the oracle;
+    dk, dv of every key through invariants that hold at any size (each row's
+    dS sums to zero over its keys, so dK sums to zero over all keys; each
+    row's P sums to one, so dV sums to the rows' dO)."""
+    from synth import WORKLOADS, bf16_bits_to_f32
+    wl = WORKLOADS["c1"]
+    say("backward c1 full size")
+    share, dout, dq, dk, dv = _run(torch_cuda, wl)
+    rows, heads = wl.sample_pairs(n_pairs=256)
+    rdq, _, _ = oracle_grads(orc, wl, rows=rows, heads=heads)
+    grad_compare(dq.cpu().numpy()[rows, heads], rdq, "c1 dq (sampled)")
+    torch = torch_cuda
+    dk_all = torch.cat(dk).double()
+    dv_all = torch.cat(dv).double()
+    ksum = dk_all.sum(0)
+    kabs = dk_all.abs().sum(0)
+    rel = float((ksum.abs() / kabs).max())
+    say("c1: max |sum_j dK_j| / sum_j |dK_j| = %.3e" % rel)
+    assert rel <= 1e-3
+    do64 = torch.from_numpy(bf16_bits_to_f32(wl.dout()).astype(np.float64)).cuda()
+    vsum = dv_all.sum(0)                      # [hkv, d]
+    want = do64.sum(0)                         # every row sees at least its own key
+    err = float((vsum - want).abs().max() / want.abs().max())
+    say("c1: max |sum_j dV_j - sum_i dO_i| / max = %.3e" % err)
+    assert err <= 1e-3
+
+
+def test_backward_deterministic_and_accumulate(torch_cuda):
+    wl = _reduced()["c4r"]
+    torch = torch_cuda
+    from context_long_sequence_amd import cpattn_partial_bwd
+    share, dout, dq, dk, dv = _run(torch, wl)
+    dq1, dk1, dv1 = dq.clone(), [x.clone() for x in dk], [x.clone() for x in dv]
+    share.backward(dout, list(wl.arrival()))
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq1) and all(torch.equal(a, b) for a, b in zip(dk, dk1))
+    assert all(torch.equal(a, b) for a, b in zip(dv, dv1))
+    # accumulate_dkv adds: a second call on the same block doubles its dk, dv (exactly: x + x)
+    b = 3
+    dqx = torch.zeros_like(dq)
+    cpattn_partial_bwd(share.q, share.k_blocks[b], share.v_blocks[b], dout, share.q_pos, share.k_pos_blocks[b],
+                       share.lse, share.delta, dqx, dk[b], dv[b], accumulate_dq=True, accumulate_dkv=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk[b], 2 * dk1[b]) and torch.equal(dv[b], 2 * dv1[b])
+
+
+def _rand_bf16(torch, shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * 0.7).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lq,lk,hq,hkv", [(100, 77, 2, 1), (257, 300, 3, 3), (33, 1, 4, 2)])
+def test_backward_ragged_random_positions(torch_cuda, orc, d, causal, lq, lk, hq, hkv):
+    """Ragged sizes (not multiples of any tile), random ascending positions,
+    GQA, one block: dq, dk, dv against the oracle."""
+    torch = torch_cuda
+    from context_long_sequence_amd import cpattn_bwd_delta, cpattn_partial, cpattn_partial_bwd
+    say("ragged d=%d causal=%d lq=%d lk=%d hq=%d hkv=%d" % (d, causal, lq, lk, hq, hkv))
+    rng = np.random.default_rng(lq * 7 + lk + d + causal)
+    qp = np.sort(rng.choice(4 * (lq + lk), lq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(4 * (lq + lk), lk, replace=False)).astype(np.int32)
+    q = _rand_bf16(torch, (lq, hq, d), 1)
+    k = _rand_bf16(torch, (lk, hkv, d), 2)
+    v = _rand_bf16(torch, (lk, hkv, d), 3)
+    dout = _rand_bf16(torch, (lq, hq, d), 4)
+    qpd, kpd = torch.from_numpy(qp).cuda(), torch.from_numpy(kp).cuda()
+    o = torch.empty((lq, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, lq), dtype=torch.float32, device="cuda")
+    cpattn_partial(q, k, v, qpd, kpd, o, lse, causal=causal)
+    delta = torch.empty((hq, lq), dtype=torch.float32, device="cuda")
+    cpattn_bwd_delta(o, dout, delta)
+    dq = torch.full((lq, hq, d), float("nan"), device="cuda")
+    dk = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    dv = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    cpattn_partial_bwd(q, k, v, dout, qpd, kpd, lse, delta, dq, dk, dv, causal=causal)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+    from synth import bf16_bits_to_f32
+    rdq, rdk, rdv, rdelta = orc.attention_grad(bits(q), bits(k), bits(v), bf16_bits_to_f32(bits(dout)), qp, kp,
+                                               None, causal)
+    grad_compare(dq.cpu().numpy(), rdq, "ragged dq")
+    grad_compare(dk.cpu().numpy(), rdk, "ragged dk")
+    grad_compare(dv.cpu().numpy(), rdv, "ragged dv")
+    # D against the oracle's <dO, O> (O here is the kernel's bf16 output: within its rounding)
+    err = float(np.max(np.abs(delta.cpu().numpy().T - rdelta)))
+    say("ragged delta: max err %.3e" % err)
+    assert err <= 2e-2 * max(1.0, float(np.max(np.abs(rdelta))))
+
+
+def test_backward_empty_and_invisible_blocks(torch_cuda):
+    """lk = 0 leaves dq as it is (accumulating) or zero; a block every key of
+    which lies after every query gets dk = dv = 0 and adds nothing to dq;
+    lq = 0 gives dk = dv = 0."""
+    torch = torch_cuda
+    from context_long_sequence_amd import cpattn_partial_bwd
+    lq, lk, hq, hkv, d = 64, 96, 2, 2, 128
+    q = _rand_bf16(torch, (lq, hq, d), 5)
+    dout = _rand_bf16(torch, (lq, hq, d), 6)
+    k = _rand_bf16(torch, (lk, hkv, d), 7)
+    v = _rand_bf16(torch, (lk, hkv, d), 8)
+    qp = torch.arange(lq, dtype=torch.int32, device="cuda")
+    kp_late = torch.arange(1000, 1000 + lk, dtype=torch.int32, device="cuda")
+    lse = torch.zeros((hq, lq), device="cuda")
+    delta = torch.zeros((hq, lq), device="cuda")
+    dq = torch.randn((lq, hq, d), device="cuda")
+    dq0 = dq.clone()
+    dk = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    dv = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    cpattn_partial_bwd(q, k, v, dout, qp, kp_late, lse, delta, dq, dk, dv, accumulate_dq=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq0) and bool((dk == 0).all()) and bool((dv == 0).all())
+    e = torch.empty((0, hkv, d), dtype=torch.bfloat16, device="cuda")
+    ef = torch.empty((0, hkv, d), device="cuda")
+    ep = torch.empty((0,), dtype=torch.int32, device="cuda")
+    cpattn_partial_bwd(q, e, e, dout, qp, ep, lse, delta, dq, ef, ef, accumulate_dq=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq0)
+    cpattn_partial_bwd(q, e, e, dout, qp, ep, lse, delta, dq, ef, ef, accumulate_dq=False)
+    torch.cuda.synchronize()
+    assert bool((dq == 0).all())
+    eq = torch.empty((0, hq, d), dtype=torch.bfloat16, device="cuda")
+    cpattn_partial_bwd(eq, k, v, eq, torch.empty((0,), dtype=torch.int32, device="cuda"), kp_late,
+                       torch.empty((hq, 0), device="cuda"), torch.empty((hq, 0), device="cuda"),
+                       torch.empty((0, hq, d), device="cuda"), dk, dv)
+    torch.cuda.synchronize()
+    assert bool((dk == 0).all()) and bool((dv == 0).all())
