@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "kernels_bwd.hpp"
 
 namespace {
 

@@ -1,0 +1,38 @@
+// kernels_bwd.hpp — host-visible launch interface of the gradient kernels
+// (partial_bwd.hip) for the C-ABI layer (api.cpp). Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+// Gradients of one KV block (partial_bwd.hip).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;           // [hq][lq], the rows' final log-normalisers
+  const float* delta;         // [hq][lq], <dO, O>
+  float* dq;                  // [lq][hq][d]
+  float* dk;                  // [lk][hkv][d]
+  float* dv;
+  const int32_t* q_pos;
+  const int32_t* k_pos;
+  const int32_t* cu_seqlens;
+  int32_t n_seqs;
+  int32_t lq, lk, hq, hkv;
+  float scale, scale_log2;
+  int32_t causal, acc_dq, acc_dkv;
+  int32_t n_tiles, n_wg;      // set per kernel by launch_bwd
+};
+
+// Enqueue the key-gradient kernel (if lk > 0) then the query-gradient kernel (if lq > 0).
+hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream);
+
+// Enqueue delta[h][i] = <dout[i][h], o[i][h]>.
+hipError_t launch_bwd_delta(const void* o, int o_bf16, const void* dout, int do_bf16, int64_t lq, int32_t hq,
+                            int32_t head_dim, float* delta, hipStream_t stream);
+
+}  // namespace cpattn

@@ -26,9 +26,9 @@
 //    and run-to-run identical results.
 //  * Each wave keeps its own side's operands in registers for the whole
 //    call (K and V of its keys, or Q and dO of its rows) and streams the
-//    other side through two LDS stages, fetched one tile ahead into
-//    registers (16-byte buffer loads; the range check zero-fills rows past
-//    the end).
+//    other side through LDS stages (three for the key kernel, two for the
+//    query kernel), fetched ahead into registers (16-byte buffer loads; the
+//    range check zero-fills rows past the end).
 //  * Orientation, with v_mfma_f32_32x32x16_bf16: the key kernel computes
 //    S = Q K^T and dP = dO V^T, so each lane holds ONE key and 16 query rows;
 //    P and dS, rounded to bf16, are then directly the B operands of
@@ -43,7 +43,7 @@
 //  * Workgroup ids are remapped so that consecutive logical tiles run on
 //    one XCD (shared L2); the tiles with the most work go first.
 #include "device_common.hpp"
-#include "kernels.hpp"
+#include "kernels_bwd.hpp"
 #include "tile_io.hpp"
 
 namespace cpattn {
@@ -127,14 +127,27 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_
 
 // ---------------------------------------------------------------------------
 // Key kernel: dK and dV of 128 keys of one KV head.
+//
+// One wave per SIMD (its accumulators alone take 128 registers), so the
+// wave's own instruction stream must overlap matrix and vector work: query
+// tiles pass through three LDS stages, and while the vector unit turns tile
+// t's scores into P and dS, the matrix unit computes S and dP of tile t+1
+// (one MFMA, then a slice of the vector work, in a fixed interleave). The S
+// and dP MFMAs alternate so that neither waits on its own previous result,
+// and every LDS operand is read a few MFMAs ahead of its use.
 
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
-  __shared__ __attribute__((aligned(1024))) char q_s0[TB], q_s1[TB], o_s0[TB], o_s1[TB];
-  __shared__ __attribute__((aligned(16))) float l_s0[32], l_s1[32], d_s0[32], d_s1[32];
-  __shared__ __attribute__((aligned(16))) int32_t p_s0[32], p_s1[32];
+  constexpr int NS = 3;   // LDS stages of query tiles
+  constexpr int RING = 4; // LDS operands in flight
+  __shared__ __attribute__((aligned(1024))) char q_s[NS][TB], o_s[NS][TB];
+  __shared__ __attribute__((aligned(16))) float l_s[NS][32], d_s[NS][32];
+  __shared__ __attribute__((aligned(16))) int32_t p_s[NS][32];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int nqt = i_hi > i_lo ? (i_hi - i_lo + 31) / 32 : 0;
   const int n_it = G * nqt;
 
-  // ---- query tiles: (head, 32 rows) per iteration, head-major ----
+  // ---- query tiles: (head, 32 rows) per iteration, head-major; tile it lives in stage it % 3 ----
   const int q_stride = p.hq * D * 2;
   u32x4_t qr[T::kUnits], orr[T::kUnits];
   float lr = 0.f, dr = 0.f;
@@ -191,12 +204,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     }
   };
   auto commit = [&](int st) __attribute__((always_inline)) {
-    commit_rows<D>(st ? (char CPATTN_LDS*)q_s1 : (char CPATTN_LDS*)q_s0, qr, tid);
-    commit_rows<D>(st ? (char CPATTN_LDS*)o_s1 : (char CPATTN_LDS*)o_s0, orr, tid);
+    commit_rows<D>((char CPATTN_LDS*)q_s[st], qr, tid);
+    commit_rows<D>((char CPATTN_LDS*)o_s[st], orr, tid);
     if (tid < 32) {
-      (st ? l_s1 : l_s0)[tid] = lr;
-      (st ? d_s1 : d_s0)[tid] = dr;
-      (st ? p_s1 : p_s0)[tid] = pr;
+      l_s[st][tid] = lr;
+      d_s[st][tid] = dr;
+      p_s[st][tid] = pr;
     }
   };
 
@@ -214,72 +227,130 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     dv_acc[dt] = f32x16_t{};
   }
 
+  // S = Q K^T and dP = dO V^T of the tile in stage st (rows: the tile's
+  // queries; column: this lane's key), alternating; work(m) runs after MFMA m.
+  auto sdp = [&](int st, f32x16_t& s, f32x16_t& dp, auto work) __attribute__((always_inline)) {
+    constexpr int NM = 2 * NQ;
+    const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
+    const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
+    auto rd = [&](int m) __attribute__((always_inline)) {
+      return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? ol : ql) + ra[m >> 1]);
+    };
+    bf16x8_t a[RING];
+#pragma unroll
+    for (int m = 0; m < RING; ++m) a[m] = rd(m);
+    s = f32x16_t{};
+    dp = f32x16_t{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], vreg[m >> 1], dp, 0, 0, 0);
+      else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], kreg[m >> 1], s, 0, 0, 0);
+      if (m + RING < NM) a[m % RING] = rd(m + RING);
+      work(m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // P = exp(s - LSE) on visible pairs and dS = P (dP - D) of rows 8rr + 4g + 0..3
+  // (registers 4rr..4rr+3), packed to bf16 pairs
+  // (the rows' LSE, D and positions are read one MFMA before the slice uses them)
+  uint32_t pp[8], pd[8];
+  f32x4 l4, d4;
+  i32x4 q4;
+  auto read_rows = [&](int st, int rr) __attribute__((always_inline)) {
+    l4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)l_s[st] + 8 * rr + 4 * g);
+    d4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)d_s[st] + 8 * rr + 4 * g);
+    q4 = p.causal ? *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g)
+                  : i32x4{0, 0, 0, 0};
+  };
+  auto softmax_rr = [&](const f32x16_t& s, const f32x16_t& dp, int rr) __attribute__((always_inline)) {
+    float pv[4], dv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bool vis = key_valid;
+      if (p.causal) {
+        vis = vis & (q4[c] >= my_kpos);
+        if (VARLEN) vis = vis & (q4[c] < my_kend);
+      }
+      pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
+      dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+    }
+    pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
+    pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
+    pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+    pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+  };
+
+  // dV^T += dO^T P and dK^T += Q^T dS for the tile in stage st, alternating
+  auto dkdv = [&](int st) __attribute__((always_inline)) {
+    constexpr int NM = 4 * NDT;   // (hf, dt, dv|dk)
+    const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
+    const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
+    auto rd = [&](int m) __attribute__((always_inline)) {
+      const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
+      return read_tr((m & 1) ? ql : ol, ta0[dt], ta8[dt], hf, T::kRowBytes);
+    };
+    const u32x4 bp[2] = {{pp[0], pp[1], pp[2], pp[3]}, {pp[4], pp[5], pp[6], pp[7]}};
+    const u32x4 bd[2] = {{pd[0], pd[1], pd[2], pd[3]}, {pd[4], pd[5], pd[6], pd[7]}};
+    bf16x8_t a[RING];
+#pragma unroll
+    for (int m = 0; m < RING; ++m) a[m] = rd(m);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
+      if (m & 1)
+        dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bd[hf]),
+                                                             dk_acc[dt], 0, 0, 0);
+      else
+        dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bp[hf]),
+                                                             dv_acc[dt], 0, 0, 0);
+      if (m + RING < NM) a[m % RING] = rd(m + RING);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   if (n_it > 0) {
     fetch(0);
     commit(0);
+    if (n_it > 1) {
+      fetch(1);
+      commit(1);
+    }
   }
   phase_barrier();
+  f32x16_t s_c = f32x16_t{}, dp_c = f32x16_t{};
+  if (n_it > 0) sdp(0, s_c, dp_c, [](int) {});
+  int st = 0;
   for (int it = 0; it < n_it; ++it) {
-    const int st = it & 1;
-    if (it + 1 < n_it) fetch(it + 1);
-    const char CPATTN_LDS* ql = st ? (const char CPATTN_LDS*)q_s1 : (const char CPATTN_LDS*)q_s0;
-    const char CPATTN_LDS* ol = st ? (const char CPATTN_LDS*)o_s1 : (const char CPATTN_LDS*)o_s0;
-    const float CPATTN_LDS* ll = st ? (const float CPATTN_LDS*)l_s1 : (const float CPATTN_LDS*)l_s0;
-    const float CPATTN_LDS* dl = st ? (const float CPATTN_LDS*)d_s1 : (const float CPATTN_LDS*)d_s0;
-    const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
-
-    // S = Q K^T, dP = dO V^T (rows: the tile's queries; column: this lane's key)
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    const int st1 = st == NS - 1 ? 0 : st + 1;
+    const int st2 = st1 == NS - 1 ? 0 : st1 + 1;
+    if (it + 2 < n_it) fetch(it + 2);
+    if (it + 1 < n_it) {
+      // the next tile's S, dP on the matrix unit (2 NQ MFMAs); this tile's P, dS in
+      // four slices between them, one after every SP MFMAs
+      constexpr int SP = NQ / 2;
+      static_assert(SP >= 2, "a slice's row reads go one MFMA ahead of it");
+      f32x16_t s_n, dp_n;
+      sdp(st1, s_n, dp_n, [&](int m) __attribute__((always_inline)) {
+        if (m % SP == SP - 2) read_rows(st, m / SP);
+        if (m % SP == SP - 1) softmax_rr(s_c, dp_c, m / SP);
+      });
+      dkdv(st);
+      s_c = s_n;
+      dp_c = dp_n;
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(ql + ra[ks]), kreg[ks], s, 0, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < NQ; ++ks)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(ol + ra[ks]), vreg[ks], dp, 0, 0, 0);
-
-    // P = exp(s - LSE) on visible pairs, dS = P (dP - D); register r is query row 8(r/4) + 4g + r%4
-    uint32_t pp[8], pd[8];
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const f32x4 l4 = *(const f32x4 CPATTN_LDS*)(ll + 8 * rr + 4 * g);
-      const f32x4 d4 = *(const f32x4 CPATTN_LDS*)(dl + 8 * rr + 4 * g);
-      i32x4 q4 = {0, 0, 0, 0};
-      if (p.causal) q4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
-      float pv[4], dv[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bool vis = key_valid;
-        if (p.causal) {
-          vis = vis & (q4[c] >= my_kpos);
-          if (VARLEN) vis = vis & (q4[c] < my_kend);
-        }
-        pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
-        dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+      for (int rr = 0; rr < 4; ++rr) {
+        read_rows(st, rr);
+        softmax_rr(s_c, dp_c, rr);
       }
-      pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
-      pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
-      pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
-      pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+      dkdv(st);
     }
-
-    // dV^T += dO^T P, dK^T += Q^T dS
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const u32x4 bp = {pp[4 * hf], pp[4 * hf + 1], pp[4 * hf + 2], pp[4 * hf + 3]};
-      const u32x4 bd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ol, ta0[dt], ta8[dt], hf, T::kRowBytes),
-                                                             __builtin_bit_cast(bf16x8_t, bp), dv_acc[dt], 0, 0, 0);
-        dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ql, ta0[dt], ta8[dt], hf, T::kRowBytes),
-                                                             __builtin_bit_cast(bf16x8_t, bd), dk_acc[dt], 0, 0, 0);
-      }
-    }
-    if (it + 1 < n_it) commit(st ^ 1);
+    if (it + 2 < n_it) commit(st2);
     phase_barrier();
+    st = st1;
   }
 
   // ---- store: lane li holds key j0 + li, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
@@ -392,14 +463,28 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
     const char CPATTN_LDS* vl = st ? (const char CPATTN_LDS*)v_s1 : (const char CPATTN_LDS*)v_s0;
     const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
 
-    // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query row)
+    // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query
+    // row), alternating so that neither chain waits on its own previous MFMA;
+    // operands read RING ahead
+    constexpr int RING = 4;
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    {
+      constexpr int NM = 2 * NQ;
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? vl : kl) + ra[m >> 1]);
+      };
+      bf16x8_t a[RING];
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(kl + ra[ks]), qreg[ks], s, 0, 0, 0);
+      for (int m = 0; m < RING; ++m) a[m] = rd(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t CPATTN_LDS*)(vl + ra[ks]), dreg[ks], dp, 0, 0, 0);
+      for (int m = 0; m < NM; ++m) {
+        if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], dreg[m >> 1], dp, 0, 0, 0);
+        else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], qreg[m >> 1], s, 0, 0, 0);
+        if (m + RING < NM) a[m % RING] = rd(m + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 
     // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile
     const int lim = min(lk - (kb + 32 * t), 32);
@@ -424,15 +509,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
       pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
     }
 
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T (K^T read transposed, RING ahead)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    {
+      constexpr int NM = 2 * NDT;  // (hf, dt)
+      const u32x4 bd[2] = {{pd[0], pd[1], pd[2], pd[3]}, {pd[4], pd[5], pd[6], pd[7]}};
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        return read_tr(kl, ta0[m % NDT], ta8[m % NDT], m / NDT, T::kRowBytes);
+      };
+      bf16x8_t a[RING];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const u32x4 bd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
+      for (int m = 0; m < RING; ++m) a[m] = rd(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kl, ta0[dt], ta8[dt], hf, T::kRowBytes),
-                                                          __builtin_bit_cast(bf16x8_t, bd), acc[dt], 0, 0, 0);
+      for (int m = 0; m < NM; ++m) {
+        acc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bd[m / NDT]),
+                                                               acc[m % NDT], 0, 0, 0);
+        if (m + RING < NM) a[m % RING] = rd(m + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (t + 1 < nt) commit(st ^ 1);
     phase_barrier();
