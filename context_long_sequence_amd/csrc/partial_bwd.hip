@@ -16,17 +16,17 @@
 // block's dK and dV are complete once every query row has been seen.
 //
 // gfx950 design (not taken from the pages, which give no kernel):
-//  * Two kernels and no atomics. The key kernel: a workgroup of four waves
-//    owns 128 keys of one KV head (32 per wave) and walks the 32-row query
-//    tiles that can see them, for every query head that reads that KV head,
-//    accumulating dK and dV in registers. The query kernel: a workgroup owns
+//  * Two kernels and no atomics. The key kernel: a workgroup of eight waves
+//    owns 128 keys of one KV head (32 per producer/consumer pair of waves)
+//    and walks the 32-row query tiles that can see them, for every query
+//    head that reads that KV head, accumulating dK and dV in registers. The query kernel: a workgroup owns
 //    128 rows (32 per wave) of one head and walks the 32-key tiles they can
 //    see, accumulating dQ. Both recompute S and dP (seven matrix products
 //    per visible pair instead of five) in exchange for no atomic traffic
 //    and run-to-run identical results.
 //  * Each wave keeps its own side's operands in registers for the whole
 //    call (K and V of its keys, or Q and dO of its rows) and streams the
-//    other side through LDS stages (three for the key kernel, two for the
+//    other side through LDS stages (four for the key kernel, two for the
 //    query kernel), fetched ahead into registers (16-byte buffer loads; the
 //    range check zero-fills rows past the end).
 //  * Orientation, with v_mfma_f32_32x32x16_bf16: the key kernel computes
@@ -128,21 +128,30 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_
 // ---------------------------------------------------------------------------
 // Key kernel: dK and dV of 128 keys of one KV head.
 //
-// One wave per SIMD (its accumulators alone take 128 registers), so the
-// wave's own instruction stream must overlap matrix and vector work: query
-// tiles pass through three LDS stages, and while the vector unit turns tile
-// t's scores into P and dS, the matrix unit computes S and dP of tile t+1
-// (one MFMA, then a slice of the vector work, in a fixed interleave). The S
-// and dP MFMAs alternate so that neither waits on its own previous result,
-// and every LDS operand is read a few MFMAs ahead of its use.
+// Eight waves in producer/consumer pairs: wave i (producer) and wave i + 4
+// (consumer) run on the same SIMD and own the same 32 keys. Per phase the
+// producer forms S = Q K^T and dP = dO V^T of query tile t (K and V of its
+// keys in registers) and turns them into P and dS, which it leaves in LDS;
+// the consumer, meanwhile, folds tile t-1's P and dS into dV^T += dO^T P and
+// dK^T += Q^T dS (its accumulators in registers). The two roles' register
+// sets are disjoint (operands vs accumulators), so each fits beside the
+// other on the SIMD, and the consumer's MFMAs run while the producer does
+// its vector work. Query tiles pass through four LDS stages (producer reads
+// tile t, consumer tile t-1, tile t+2 is being written).
+
+constexpr int kDkvThreads = 512;   // four producer and four consumer waves
 
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
-  constexpr int NS = 3;   // LDS stages of query tiles
-  constexpr int RING = 4; // LDS operands in flight
+  constexpr int NS = 4;                     // LDS stages of query tiles
+  constexpr int RING = 4;                   // LDS operands in flight
+  constexpr int U = TB / 16;                // 16-byte units of one tile
+  constexpr int NU = 2 * U / kDkvThreads;   // units of the (Q, dO) pair per thread
+  static_assert(NU >= 1 && (2 * U) % kDkvThreads == 0, "the pair of tiles splits evenly over the threads");
   __shared__ __attribute__((aligned(1024))) char q_s[NS][TB], o_s[NS][TB];
+  __shared__ __attribute__((aligned(1024))) char x_s[2][4][4][1024];  // [buffer][key block][part][lane]
   __shared__ __attribute__((aligned(16))) float l_s[NS][32], d_s[NS][32];
   __shared__ __attribute__((aligned(16))) int32_t p_s[NS][32];
   typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -152,6 +161,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < 4;
+  const int kw = wave & 3;                  // the wave's 32-key block
   const int g = lane >> 5, li = lane & 31;
   const int L = xcd_remap(blockIdx.x, p.n_wg);
   const int hk = L / p.n_tiles;
@@ -159,23 +170,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int G = p.hq / p.hkv;
   const int lq = p.lq, lk = p.lk;
   const int wg_j0 = kt * 128, wg_j1 = min(wg_j0 + 128, lk);
-  const int j0 = wg_j0 + 32 * wave;
+  const int j0 = wg_j0 + 32 * kw;
   const int kj = min(j0 + li, lk - 1);              // this lane's key (clamped)
   const bool key_valid = j0 + li < lk;
 
-  // the wave's keys: B operands of S = Q K^T and dP = dO V^T
-  bf16x8_t kreg[NQ], vreg[NQ];
-  {
-    const int64_t off = ((int64_t)kj * p.hkv + hk) * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < NQ; ++ks) {
-      kreg[ks] = *(const bf16x8_t*)((const __bf16*)p.k + off + 16 * ks);
-      vreg[ks] = *(const bf16x8_t*)((const __bf16*)p.v + off + 16 * ks);
-    }
-  }
-  // rows that see key j: q_pos >= k_pos[j] and, with documents, q_pos < end of k's document
-  const int32_t my_kpos = p.causal ? p.k_pos[kj] : 0;
-  const int32_t my_kend = VARLEN ? doc_end(p.cu_seqlens, p.n_seqs, my_kpos) : 0;
+  // rows that see the workgroup's keys
   int i_lo = 0, i_hi = lq;
   if (p.causal) {
     i_lo = wave_upper_bound(p.q_pos, lq, p.k_pos[wg_j0] - 1);
@@ -184,16 +183,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int nqt = i_hi > i_lo ? (i_hi - i_lo + 31) / 32 : 0;
   const int n_it = G * nqt;
 
-  // ---- query tiles: (head, 32 rows) per iteration, head-major; tile it lives in stage it % 3 ----
+  // ---- query tiles: (head, 32 rows) per iteration, head-major; tile t lives in stage t % 4 ----
+  // thread t moves 16-byte units t, t + 512, ... of the pair (Q tile, dO tile)
   const int q_stride = p.hq * D * 2;
-  u32x4_t qr[T::kUnits], orr[T::kUnits];
+  u32x4_t xr[NU];
   float lr = 0.f, dr = 0.f;
   int32_t pr = 0;
   auto fetch = [&](int it) __attribute__((always_inline)) {
     const int hh = hk * G + it / nqt;
     const int i0 = i_lo + 32 * (it % nqt);
-    fetch_rows<D>(qr, (const char*)p.q + (int64_t)hh * D * 2, q_stride, i0, lq, tid);
-    fetch_rows<D>(orr, (const char*)p.dout + (int64_t)hh * D * 2, q_stride, i0, lq, tid);
+    const int rows = clamp_rows(lq - i0, 32);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int unit = tid + kDkvThreads * u;
+      const bool is_o = unit >= U;                     // wave-uniform
+      const int lu = is_o ? unit - U : unit;
+      const char* base = (const char*)(is_o ? p.dout : p.q) + (int64_t)hh * D * 2 + (int64_t)i0 * q_stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (int64_t)rows * q_stride);
+      xr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lu / T::kChunks) * q_stride + (lu % T::kChunks) * 16, 0, 0);
+    }
     if (tid < 32) {
       const int i = i0 + tid;
       const bool ok = i < lq;
@@ -204,110 +212,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     }
   };
   auto commit = [&](int st) __attribute__((always_inline)) {
-    commit_rows<D>((char CPATTN_LDS*)q_s[st], qr, tid);
-    commit_rows<D>((char CPATTN_LDS*)o_s[st], orr, tid);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int unit = tid + kDkvThreads * u;
+      const bool is_o = unit >= U;
+      const int lu = is_o ? unit - U : unit;
+      char CPATTN_LDS* tile = (char CPATTN_LDS*)(is_o ? o_s[st] : q_s[st]);
+      *(u32x4_t CPATTN_LDS*)(tile + T::off(lu / T::kChunks, lu % T::kChunks)) = xr[u];
+    }
     if (tid < 32) {
       l_s[st][tid] = lr;
       d_s[st][tid] = dr;
       p_s[st][tid] = pr;
-    }
-  };
-
-  int ra[NQ];         // row reads: row li, chunk 2ks + g
-#pragma unroll
-  for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
-  int ta0[NDT], ta8[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) tr_offsets<D>(lane, dt, ta0[dt], ta8[dt]);
-
-  f32x16_t dk_acc[NDT], dv_acc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    dk_acc[dt] = f32x16_t{};
-    dv_acc[dt] = f32x16_t{};
-  }
-
-  // S = Q K^T and dP = dO V^T of the tile in stage st (rows: the tile's
-  // queries; column: this lane's key), alternating; work(m) runs after MFMA m.
-  auto sdp = [&](int st, f32x16_t& s, f32x16_t& dp, auto work) __attribute__((always_inline)) {
-    constexpr int NM = 2 * NQ;
-    const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
-    const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
-    auto rd = [&](int m) __attribute__((always_inline)) {
-      return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? ol : ql) + ra[m >> 1]);
-    };
-    bf16x8_t a[RING];
-#pragma unroll
-    for (int m = 0; m < RING; ++m) a[m] = rd(m);
-    s = f32x16_t{};
-    dp = f32x16_t{};
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], vreg[m >> 1], dp, 0, 0, 0);
-      else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], kreg[m >> 1], s, 0, 0, 0);
-      if (m + RING < NM) a[m % RING] = rd(m + RING);
-      work(m);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // P = exp(s - LSE) on visible pairs and dS = P (dP - D) of rows 8rr + 4g + 0..3
-  // (registers 4rr..4rr+3), packed to bf16 pairs
-  // (the rows' LSE, D and positions are read one MFMA before the slice uses them)
-  uint32_t pp[8], pd[8];
-  f32x4 l4, d4;
-  i32x4 q4;
-  auto read_rows = [&](int st, int rr) __attribute__((always_inline)) {
-    l4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)l_s[st] + 8 * rr + 4 * g);
-    d4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)d_s[st] + 8 * rr + 4 * g);
-    q4 = p.causal ? *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g)
-                  : i32x4{0, 0, 0, 0};
-  };
-  auto softmax_rr = [&](const f32x16_t& s, const f32x16_t& dp, int rr) __attribute__((always_inline)) {
-    float pv[4], dv[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bool vis = key_valid;
-      if (p.causal) {
-        vis = vis & (q4[c] >= my_kpos);
-        if (VARLEN) vis = vis & (q4[c] < my_kend);
-      }
-      pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
-      dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
-    }
-    pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
-    pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
-    pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
-    pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
-  };
-
-  // dV^T += dO^T P and dK^T += Q^T dS for the tile in stage st, alternating
-  auto dkdv = [&](int st) __attribute__((always_inline)) {
-    constexpr int NM = 4 * NDT;   // (hf, dt, dv|dk)
-    const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
-    const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
-    auto rd = [&](int m) __attribute__((always_inline)) {
-      const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
-      return read_tr((m & 1) ? ql : ol, ta0[dt], ta8[dt], hf, T::kRowBytes);
-    };
-    const u32x4 bp[2] = {{pp[0], pp[1], pp[2], pp[3]}, {pp[4], pp[5], pp[6], pp[7]}};
-    const u32x4 bd[2] = {{pd[0], pd[1], pd[2], pd[3]}, {pd[4], pd[5], pd[6], pd[7]}};
-    bf16x8_t a[RING];
-#pragma unroll
-    for (int m = 0; m < RING; ++m) a[m] = rd(m);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
-      if (m & 1)
-        dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bd[hf]),
-                                                             dk_acc[dt], 0, 0, 0);
-      else
-        dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bp[hf]),
-                                                             dv_acc[dt], 0, 0, 0);
-      if (m + RING < NM) a[m % RING] = rd(m + RING);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -320,37 +236,131 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     }
   }
   phase_barrier();
-  f32x16_t s_c = f32x16_t{}, dp_c = f32x16_t{};
-  if (n_it > 0) sdp(0, s_c, dp_c, [](int) {});
-  int st = 0;
-  for (int it = 0; it < n_it; ++it) {
-    const int st1 = st == NS - 1 ? 0 : st + 1;
-    const int st2 = st1 == NS - 1 ? 0 : st1 + 1;
-    if (it + 2 < n_it) fetch(it + 2);
-    if (it + 1 < n_it) {
-      // the next tile's S, dP on the matrix unit (2 NQ MFMAs); this tile's P, dS in
-      // four slices between them, one after every SP MFMAs
-      constexpr int SP = NQ / 2;
-      static_assert(SP >= 2, "a slice's row reads go one MFMA ahead of it");
-      f32x16_t s_n, dp_n;
-      sdp(st1, s_n, dp_n, [&](int m) __attribute__((always_inline)) {
-        if (m % SP == SP - 2) read_rows(st, m / SP);
-        if (m % SP == SP - 1) softmax_rr(s_c, dp_c, m / SP);
-      });
-      dkdv(st);
-      s_c = s_n;
-      dp_c = dp_n;
-    } else {
+
+  if (producer) {
+    // ---------------- producer: S, dP -> P, dS ----------------
+    bf16x8_t kreg[NQ], vreg[NQ];  // B operands of S = Q K^T and dP = dO V^T
+    {
+      const int64_t off = ((int64_t)kj * p.hkv + hk) * D + 8 * g;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        read_rows(st, rr);
-        softmax_rr(s_c, dp_c, rr);
+      for (int ks = 0; ks < NQ; ++ks) {
+        kreg[ks] = *(const bf16x8_t*)((const __bf16*)p.k + off + 16 * ks);
+        vreg[ks] = *(const bf16x8_t*)((const __bf16*)p.v + off + 16 * ks);
       }
-      dkdv(st);
     }
-    if (it + 2 < n_it) commit(st2);
+    // a query row sees key j iff q_pos >= k_pos[j] and, with documents, q_pos < end of k's document
+    const int32_t my_kpos = p.causal ? p.k_pos[kj] : 0;
+    const int32_t my_kend = VARLEN ? doc_end(p.cu_seqlens, p.n_seqs, my_kpos) : 0;
+    int ra[NQ];  // row reads: row li, chunk 2ks + g
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
+    int st = 0;
+    for (int k = 0; k <= n_it; ++k) {
+      if (k + 2 < n_it) fetch(k + 2);
+      if (k < n_it) {
+        // S and dP of tile k (rows: the tile's queries; column: this lane's key), alternating
+        const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
+        const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+        {
+          constexpr int NM = 2 * NQ;
+          auto rd = [&](int m) __attribute__((always_inline)) {
+            return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? ol : ql) + ra[m >> 1]);
+          };
+          bf16x8_t a[RING];
+#pragma unroll
+          for (int m = 0; m < RING; ++m) a[m] = rd(m);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], vreg[m >> 1], dp, 0, 0, 0);
+            else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], kreg[m >> 1], s, 0, 0, 0);
+            if (m + RING < NM) a[m % RING] = rd(m + RING);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // P = exp(s - LSE) on visible pairs, dS = P (dP - D); register r is query row
+        // 8(r/4) + 4g + r%4; packed to bf16 pairs and left in LDS for the consumer
+        uint32_t pp[8], pd[8];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 l4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)l_s[st] + 8 * rr + 4 * g);
+          const f32x4 d4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)d_s[st] + 8 * rr + 4 * g);
+          i32x4 q4 = {0, 0, 0, 0};
+          if (p.causal) q4 = *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g);
+          float pv[4], dv[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bool vis = key_valid;
+            if (p.causal) {
+              vis = vis & (q4[c] >= my_kpos);
+              if (VARLEN) vis = vis & (q4[c] < my_kend);
+            }
+            pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
+            dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+          }
+          pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
+          pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
+          pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+          pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+        }
+        char CPATTN_LDS* xb = (char CPATTN_LDS*)x_s[k & 1][kw] + 16 * lane;
+        *(u32x4 CPATTN_LDS*)(xb) = u32x4{pp[0], pp[1], pp[2], pp[3]};
+        *(u32x4 CPATTN_LDS*)(xb + 1024) = u32x4{pp[4], pp[5], pp[6], pp[7]};
+        *(u32x4 CPATTN_LDS*)(xb + 2048) = u32x4{pd[0], pd[1], pd[2], pd[3]};
+        *(u32x4 CPATTN_LDS*)(xb + 3072) = u32x4{pd[4], pd[5], pd[6], pd[7]};
+      }
+      if (k + 2 < n_it) commit((st + 2) & (NS - 1));  // stage (k + 2) % 4; st is k % 4
+      phase_barrier();
+      st = (st + 1) & (NS - 1);
+    }
+    return;
+  }
+
+  // ---------------- consumer: dV^T += dO^T P, dK^T += Q^T dS ----------------
+  int ta0[NDT], ta8[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) tr_offsets<D>(lane, dt, ta0[dt], ta8[dt]);
+  f32x16_t dk_acc[NDT], dv_acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk_acc[dt] = f32x16_t{};
+    dv_acc[dt] = f32x16_t{};
+  }
+  int st = NS - 1;  // stage of tile k - 1
+  for (int k = 0; k <= n_it; ++k) {
+    if (k + 2 < n_it) fetch(k + 2);
+    if (k >= 1) {
+      const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
+      const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
+      const char CPATTN_LDS* xb = (const char CPATTN_LDS*)x_s[(k - 1) & 1][kw] + 16 * lane;
+      const u32x4 bp0 = *(const u32x4 CPATTN_LDS*)(xb), bp1 = *(const u32x4 CPATTN_LDS*)(xb + 1024);
+      const u32x4 bd0 = *(const u32x4 CPATTN_LDS*)(xb + 2048), bd1 = *(const u32x4 CPATTN_LDS*)(xb + 3072);
+      constexpr int NM = 4 * NDT;   // (hf, dt, dv|dk)
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
+        return read_tr((m & 1) ? ql : ol, ta0[dt], ta8[dt], hf, T::kRowBytes);
+      };
+      bf16x8_t a[RING];
+#pragma unroll
+      for (int m = 0; m < RING; ++m) a[m] = rd(m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int hf = m / (2 * NDT), dt = (m >> 1) % NDT;
+        if (m & 1)
+          dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, hf ? bd1 : bd0),
+                                                               dk_acc[dt], 0, 0, 0);
+        else
+          dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, hf ? bp1 : bp0),
+                                                               dv_acc[dt], 0, 0, 0);
+        if (m + RING < NM) a[m % RING] = rd(m + RING);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (k + 2 < n_it) commit((st + 3) & (NS - 1));  // stage (k + 2) % 4; st is (k - 1) % 4
     phase_barrier();
-    st = st1;
+    st = (st + 1) & (NS - 1);
   }
 
   // ---- store: lane li holds key j0 + li, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
@@ -588,7 +598,7 @@ static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {
     BwdParams a = p;
     a.n_tiles = (p.lk + 127) / 128;
     a.n_wg = a.n_tiles * p.hkv;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kDkvThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
