@@ -42,6 +42,8 @@
 //    transposed reads (4 rows x 4 chunks) free of bank conflicts.
 //  * Workgroup ids are remapped so that consecutive logical tiles run on
 //    one XCD (shared L2); the tiles with the most work go first.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels_bwd.hpp"
 #include "tile_io.hpp"
@@ -130,14 +132,15 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_
 //
 // Eight waves in producer/consumer pairs: wave i (producer) and wave i + 4
 // (consumer) run on the same SIMD and own the same 32 keys. Per phase the
-// producer forms S = Q K^T and dP = dO V^T of query tile t (K and V of its
-// keys in registers) and turns them into P and dS, which it leaves in LDS;
+// producer turns S = Q K^T and dP = dO V^T of query tile t (K and V of its
+// keys in registers) into P and dS, which it leaves in LDS, while its MFMAs
+// already form S and dP of tile t+1;
 // the consumer, meanwhile, folds tile t-1's P and dS into dV^T += dO^T P and
 // dK^T += Q^T dS (its accumulators in registers). The two roles' register
 // sets are disjoint (operands vs accumulators), so each fits beside the
 // other on the SIMD, and the consumer's MFMAs run while the producer does
-// its vector work. Query tiles pass through four LDS stages (producer reads
-// tile t, consumer tile t-1, tile t+2 is being written).
+// its vector work. Query tiles pass through four LDS stages (the producer
+// reads tiles t and t+1, the consumer tile t-1, tile t+2 is being written).
 
 constexpr int kDkvThreads = 512;   // four producer and four consumer waves
 
@@ -184,15 +187,25 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int n_it = G * nqt;
 
   // ---- query tiles: (head, 32 rows) per iteration, head-major; tile t lives in stage t % 4 ----
-  // thread t moves 16-byte units t, t + 512, ... of the pair (Q tile, dO tile)
+  // Thread t moves 16-byte units t, t + 512, ... of the pair (Q tile, dO tile).
+  // Tile t+3 is fetched into registers (set (t+3) % 2) in phase t and written to
+  // LDS at the end of phase t+1, so a load has two phases to arrive. The fetch
+  // is issued in every phase, reading nothing past the last tile, so that the
+  // compiler's count of loads in flight is the same on every path and its wait
+  // before a commit covers only the older set.
   const int q_stride = p.hq * D * 2;
-  u32x4_t xr[NU];
-  float lr = 0.f, dr = 0.f;
-  int32_t pr = 0;
-  auto fetch = [&](int it) __attribute__((always_inline)) {
-    const int hh = hk * G + it / nqt;
-    const int i0 = i_lo + 32 * (it % nqt);
-    const int rows = clamp_rows(lq - i0, 32);
+  u32x4_t xr[2][NU];
+  float lr[2] = {0.f, 0.f}, dr[2] = {0.f, 0.f};
+  int32_t pr[2] = {0, 0};
+  int nr[2] = {0, 0};  // rows of the fetched tile inside the tensor
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto fetch = [&](int it, auto set) __attribute__((always_inline)) {
+    constexpr int e = decltype(set)::value;
+    const bool live = it < n_it;
+    const int hh = hk * G + (live ? it / nqt : 0);
+    const int i0 = live ? i_lo + 32 * (it % nqt) : lq;
+    const int rows = clamp_rows(lq - i0, 32);          // 0 past the last tile: nothing is read
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int unit = tid + kDkvThreads * u;
@@ -200,41 +213,44 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       const int lu = is_o ? unit - U : unit;
       const char* base = (const char*)(is_o ? p.dout : p.q) + (int64_t)hh * D * 2 + (int64_t)i0 * q_stride;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (int64_t)rows * q_stride);
-      xr[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lu / T::kChunks) * q_stride + (lu % T::kChunks) * 16, 0, 0);
+      xr[e][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lu / T::kChunks) * q_stride + (lu % T::kChunks) * 16,
+                                                       0, 0);
     }
-    if (tid < 32) {
-      const int i = i0 + tid;
-      const bool ok = i < lq;
-      const float l = ok ? p.lse[(int64_t)hh * lq + i] : neg_inf();
-      lr = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // rows past the end, or that see nothing: P = 0
-      dr = ok ? p.delta[(int64_t)hh * lq + i] : 0.f;
-      pr = (ok && p.causal) ? p.q_pos[i] : (int32_t)0x80000000;
-    }
+    // The rows' LSE, D and positions: lanes 0..31 of wave 0 read them. Every wave
+    // issues the same loads (the range is empty elsewhere and they read nothing),
+    // so that all waves have the same loads in flight; row validity and the
+    // base-2 conversion are applied at the commit, so nothing waits here.
+    const int mine = wave == 0 ? rows : 0;
+    nr[e] = rows;
+    const int64_t lo = (int64_t)hh * lq + i0;
+    lr[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lse + lo, mine * 4), lane * 4, 0, 0));
+    dr[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.delta + lo, mine * 4), lane * 4, 0, 0));
+    pr[e] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.q_pos + i0, p.causal ? mine * 4 : 0), lane * 4, 0, 0);
   };
-  auto commit = [&](int st) __attribute__((always_inline)) {
+  auto commit = [&](int st, auto set) __attribute__((always_inline)) {
+    constexpr int e = decltype(set)::value;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int unit = tid + kDkvThreads * u;
       const bool is_o = unit >= U;
       const int lu = is_o ? unit - U : unit;
       char CPATTN_LDS* tile = (char CPATTN_LDS*)(is_o ? o_s[st] : q_s[st]);
-      *(u32x4_t CPATTN_LDS*)(tile + T::off(lu / T::kChunks, lu % T::kChunks)) = xr[u];
+      *(u32x4_t CPATTN_LDS*)(tile + T::off(lu / T::kChunks, lu % T::kChunks)) = xr[e][u];
     }
     if (tid < 32) {
-      l_s[st][tid] = lr;
-      d_s[st][tid] = dr;
-      p_s[st][tid] = pr;
+      // base-2 LSE; rows past the end, or that see nothing, get +inf: P = 0
+      const bool ok = tid < nr[e];
+      l_s[st][tid] = (!ok || lr[e] == neg_inf()) ? __builtin_inff() : lr[e] * kLog2e;
+      d_s[st][tid] = ok ? dr[e] : 0.f;
+      p_s[st][tid] = (ok && p.causal) ? pr[e] : (int32_t)0x80000000;
     }
   };
 
-  if (n_it > 0) {
-    fetch(0);
-    commit(0);
-    if (n_it > 1) {
-      fetch(1);
-      commit(1);
-    }
-  }
+  fetch(0, P0{});
+  commit(0, P0{});
+  fetch(1, P1{});
+  commit(1, P1{});
+  fetch(2, P0{});
   phase_barrier();
 
   if (producer) {
@@ -254,55 +270,86 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     int ra[NQ];  // row reads: row li, chunk 2ks + g
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
-    int st = 0;
-    for (int k = 0; k <= n_it; ++k) {
-      if (k + 2 < n_it) fetch(k + 2);
-      if (k < n_it) {
-        // S and dP of tile k (rows: the tile's queries; column: this lane's key), alternating
-        const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
-        const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-        {
-          constexpr int NM = 2 * NQ;
-          auto rd = [&](int m) __attribute__((always_inline)) {
-            return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? ol : ql) + ra[m >> 1]);
-          };
-          bf16x8_t a[RING];
+    // S and dP of the tile in stage st (rows: the tile's queries; column: this
+    // lane's key), alternating; work(m) runs after MFMA m
+    auto sdp = [&](int st, f32x16_t& s, f32x16_t& dp, auto work) __attribute__((always_inline)) {
+      constexpr int NM = 2 * NQ;
+      const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
+      const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? ol : ql) + ra[m >> 1]);
+      };
+      bf16x8_t a[RING];
 #pragma unroll
-          for (int m = 0; m < RING; ++m) a[m] = rd(m);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < RING; ++m) a[m] = rd(m);
+      s = f32x16_t{};
+      dp = f32x16_t{};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], vreg[m >> 1], dp, 0, 0, 0);
-            else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], kreg[m >> 1], s, 0, 0, 0);
-            if (m + RING < NM) a[m % RING] = rd(m + RING);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int m = 0; m < NM; ++m) {
+        if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], vreg[m >> 1], dp, 0, 0, 0);
+        else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], kreg[m >> 1], s, 0, 0, 0);
+        if (m + RING < NM) a[m % RING] = rd(m + RING);
+        work(m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // P = exp(s - LSE) on visible pairs, dS = P (dP - D) of rows 8rr + 4g + 0..3
+    // (registers 4rr..4rr+3), packed to bf16 pairs; the rows' LSE, D and
+    // positions are read one MFMA before the slice that uses them
+    uint32_t pp[8], pd[8];
+    f32x4 l4, d4;
+    i32x4 q4;
+    auto read_rows = [&](int st, int rr) __attribute__((always_inline)) {
+      l4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)l_s[st] + 8 * rr + 4 * g);
+      d4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)d_s[st] + 8 * rr + 4 * g);
+      q4 = p.causal ? *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g)
+                    : i32x4{0, 0, 0, 0};
+    };
+    auto softmax_rr = [&](const f32x16_t& s, const f32x16_t& dp, int rr) __attribute__((always_inline)) {
+      float pv[4], dv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bool vis = key_valid;
+        if (p.causal) {
+          vis = vis & (q4[c] >= my_kpos);
+          if (VARLEN) vis = vis & (q4[c] < my_kend);
         }
-        // P = exp(s - LSE) on visible pairs, dS = P (dP - D); register r is query row
-        // 8(r/4) + 4g + r%4; packed to bf16 pairs and left in LDS for the consumer
-        uint32_t pp[8], pd[8];
+        pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
+        dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+      }
+      pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
+      pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
+      pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+      pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+    };
+    // Phase k: P, dS of tile k (its S, dP formed in phase k - 1) in four slices
+    // placed between the MFMAs of tile k+1's S, dP, so that the wave's vector
+    // work overlaps its own matrix work.
+    f32x16_t s_c = f32x16_t{}, dp_c = f32x16_t{};
+    if (n_it > 0) sdp(0, s_c, dp_c, [](int) {});
+    int st = 0;
+    // phase k fetches tile k+3 into set fs = (k+3) % 2 and commits tile k+2 from set cs = (k+2) % 2
+    auto phase = [&](int k, auto fs, auto cs) __attribute__((always_inline)) {
+      fetch(k + 3, fs);
+      if (k < n_it) {
+        const int st1 = (st + 1) & (NS - 1);
+        if (k + 1 < n_it) {
+          constexpr int SP = NQ / 2;  // MFMAs per slice
+          static_assert(SP >= 2, "a slice's row reads go one MFMA ahead of it");
+          f32x16_t s_n, dp_n;
+          sdp(st1, s_n, dp_n, [&](int m) __attribute__((always_inline)) {
+            if (m % SP == SP - 2) read_rows(st, m / SP);
+            if (m % SP == SP - 1) softmax_rr(s_c, dp_c, m / SP);
+          });
+          s_c = s_n;
+          dp_c = dp_n;
+        } else {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const f32x4 l4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)l_s[st] + 8 * rr + 4 * g);
-          const f32x4 d4 = *(const f32x4 CPATTN_LDS*)((const float CPATTN_LDS*)d_s[st] + 8 * rr + 4 * g);
-          i32x4 q4 = {0, 0, 0, 0};
-          if (p.causal) q4 = *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g);
-          float pv[4], dv[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bool vis = key_valid;
-            if (p.causal) {
-              vis = vis & (q4[c] >= my_kpos);
-              if (VARLEN) vis = vis & (q4[c] < my_kend);
-            }
-            pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
-            dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
+          for (int rr = 0; rr < 4; ++rr) {
+            read_rows(st, rr);
+            softmax_rr(s_c, dp_c, rr);
           }
-          pp[2 * rr] = pack_bf16x2(pv[0], pv[1]);
-          pp[2 * rr + 1] = pack_bf16x2(pv[2], pv[3]);
-          pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
-          pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
         }
         char CPATTN_LDS* xb = (char CPATTN_LDS*)x_s[k & 1][kw] + 16 * lane;
         *(u32x4 CPATTN_LDS*)(xb) = u32x4{pp[0], pp[1], pp[2], pp[3]};
@@ -310,9 +357,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
         *(u32x4 CPATTN_LDS*)(xb + 2048) = u32x4{pd[0], pd[1], pd[2], pd[3]};
         *(u32x4 CPATTN_LDS*)(xb + 3072) = u32x4{pd[4], pd[5], pd[6], pd[7]};
       }
-      if (k + 2 < n_it) commit((st + 2) & (NS - 1));  // stage (k + 2) % 4; st is k % 4
+      if (k + 2 < n_it) commit((st + 2) & (NS - 1), cs);  // stage (k + 2) % 4; st is k % 4
       phase_barrier();
       st = (st + 1) & (NS - 1);
+    };
+    for (int k = 0; k <= n_it; k += 2) {
+      phase(k, P1{}, P0{});
+      if (k + 1 <= n_it) phase(k + 1, P0{}, P1{});
     }
     return;
   }
@@ -328,8 +379,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     dv_acc[dt] = f32x16_t{};
   }
   int st = NS - 1;  // stage of tile k - 1
-  for (int k = 0; k <= n_it; ++k) {
-    if (k + 2 < n_it) fetch(k + 2);
+  auto phase = [&](int k, auto fs, auto cs) __attribute__((always_inline)) {
+    fetch(k + 3, fs);
     if (k >= 1) {
       const char CPATTN_LDS* ql = (const char CPATTN_LDS*)q_s[st];
       const char CPATTN_LDS* ol = (const char CPATTN_LDS*)o_s[st];
@@ -358,9 +409,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (k + 2 < n_it) commit((st + 3) & (NS - 1));  // stage (k + 2) % 4; st is (k - 1) % 4
+    if (k + 2 < n_it) commit((st + 3) & (NS - 1), cs);  // stage (k + 2) % 4; st is (k - 1) % 4
     phase_barrier();
     st = (st + 1) & (NS - 1);
+  };
+  for (int k = 0; k <= n_it; k += 2) {
+    phase(k, P1{}, P0{});
+    if (k + 1 <= n_it) phase(k + 1, P0{}, P1{});
   }
 
   // ---- store: lane li holds key j0 + li, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
