@@ -151,8 +151,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   constexpr int NS = 4;                     // LDS stages of query tiles
   constexpr int RING = 4;                   // LDS operands in flight
   constexpr int U = TB / 16;                // 16-byte units of one tile
-  constexpr int NU = 2 * U / kDkvThreads;   // units of the (Q, dO) pair per thread
-  static_assert(NU >= 1 && (2 * U) % kDkvThreads == 0, "the pair of tiles splits evenly over the threads");
+  constexpr int FT = kDkvThreads / 2;       // the consumer waves move the query tiles
+  constexpr int NU = 2 * U / FT;            // units of the (Q, dO) pair per consumer thread
+  static_assert(NU >= 1 && (2 * U) % FT == 0, "the pair of tiles splits evenly over the consumer threads");
   __shared__ __attribute__((aligned(1024))) char q_s[NS][TB], o_s[NS][TB];
   __shared__ __attribute__((aligned(1024))) char x_s[2][4][4][1024];  // [buffer][key block][part][lane]
   __shared__ __attribute__((aligned(16))) float l_s[NS][32], d_s[NS][32];
@@ -187,7 +188,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int n_it = G * nqt;
 
   // ---- query tiles: (head, 32 rows) per iteration, head-major; tile t lives in stage t % 4 ----
-  // Thread t moves 16-byte units t, t + 512, ... of the pair (Q tile, dO tile).
+  // The consumer waves (whose per-phase work is the lighter) move the tiles:
+  // consumer thread c = tid - 256 moves 16-byte units c, c + 256, ... of the
+  // pair (Q tile, dO tile); the producers only compute.
+  const int ct = tid - FT;
   // Tile t+3 is fetched into registers (set (t+3) % 2) in phase t and written to
   // LDS at the end of phase t+1, so a load has two phases to arrive. The fetch
   // is issued in every phase, reading nothing past the last tile, so that the
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     const int rows = clamp_rows(lq - i0, 32);          // 0 past the last tile: nothing is read
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = tid + kDkvThreads * u;
+      const int unit = ct + FT * u;
       const bool is_o = unit >= U;                     // wave-uniform
       const int lu = is_o ? unit - U : unit;
       const char* base = (const char*)(is_o ? p.dout : p.q) + (int64_t)hh * D * 2 + (int64_t)i0 * q_stride;
@@ -216,11 +220,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       xr[e][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lu / T::kChunks) * q_stride + (lu % T::kChunks) * 16,
                                                        0, 0);
     }
-    // The rows' LSE, D and positions: lanes 0..31 of wave 0 read them. Every wave
-    // issues the same loads (the range is empty elsewhere and they read nothing),
-    // so that all waves have the same loads in flight; row validity and the
-    // base-2 conversion are applied at the commit, so nothing waits here.
-    const int mine = wave == 0 ? rows : 0;
+    // The rows' LSE, D and positions: lanes 0..31 of wave 4 read them. Every
+    // consumer wave issues the same loads (the range is empty elsewhere and they
+    // read nothing), so that all have the same loads in flight; row validity and
+    // the base-2 conversion are applied at the commit, so nothing waits here.
+    const int mine = wave == 4 ? rows : 0;
     nr[e] = rows;
     const int64_t lo = (int64_t)hh * lq + i0;
     lr[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lse + lo, mine * 4), lane * 4, 0, 0));
@@ -231,26 +235,28 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     constexpr int e = decltype(set)::value;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = tid + kDkvThreads * u;
+      const int unit = ct + FT * u;
       const bool is_o = unit >= U;
       const int lu = is_o ? unit - U : unit;
       char CPATTN_LDS* tile = (char CPATTN_LDS*)(is_o ? o_s[st] : q_s[st]);
       *(u32x4_t CPATTN_LDS*)(tile + T::off(lu / T::kChunks, lu % T::kChunks)) = xr[e][u];
     }
-    if (tid < 32) {
+    if (ct >= 0 && ct < 32) {
       // base-2 LSE; rows past the end, or that see nothing, get +inf: P = 0
-      const bool ok = tid < nr[e];
-      l_s[st][tid] = (!ok || lr[e] == neg_inf()) ? __builtin_inff() : lr[e] * kLog2e;
-      d_s[st][tid] = ok ? dr[e] : 0.f;
-      p_s[st][tid] = (ok && p.causal) ? pr[e] : (int32_t)0x80000000;
+      const bool ok = ct < nr[e];
+      l_s[st][ct] = (!ok || lr[e] == neg_inf()) ? __builtin_inff() : lr[e] * kLog2e;
+      d_s[st][ct] = ok ? dr[e] : 0.f;
+      p_s[st][ct] = (ok && p.causal) ? pr[e] : (int32_t)0x80000000;
     }
   };
 
-  fetch(0, P0{});
-  commit(0, P0{});
-  fetch(1, P1{});
-  commit(1, P1{});
-  fetch(2, P0{});
+  if (!producer) {
+    fetch(0, P0{});
+    commit(0, P0{});
+    fetch(1, P1{});
+    commit(1, P1{});
+    fetch(2, P0{});
+  }
   phase_barrier();
 
   if (producer) {
@@ -331,7 +337,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     int st = 0;
     // phase k fetches tile k+3 into set fs = (k+3) % 2 and commits tile k+2 from set cs = (k+2) % 2
     auto phase = [&](int k, auto fs, auto cs) __attribute__((always_inline)) {
-      fetch(k + 3, fs);
+      (void)fs;
+      (void)cs;
       if (k < n_it) {
         const int st1 = (st + 1) & (NS - 1);
         if (k + 1 < n_it) {
@@ -357,7 +364,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
         *(u32x4 CPATTN_LDS*)(xb + 2048) = u32x4{pd[0], pd[1], pd[2], pd[3]};
         *(u32x4 CPATTN_LDS*)(xb + 3072) = u32x4{pd[4], pd[5], pd[6], pd[7]};
       }
-      if (k + 2 < n_it) commit((st + 2) & (NS - 1), cs);  // stage (k + 2) % 4; st is k % 4
       phase_barrier();
       st = (st + 1) & (NS - 1);
     };
