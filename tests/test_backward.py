@@ -117,33 +117,43 @@ def test_backward_reduced_all(torch_cuda, orc, name):
     grad_compare(np.concatenate([x.cpu().numpy() for x in dv]), np.concatenate(rdv), name + " dv")
 
 
-def test_backward_full_size_c1_sampled(torch_cuda, orc):
-    """The 64K-token zig-zag cp8 rank share at full size, in the launch
-    configuration the benchmark times: dq on sampled rows against the oracle;
-    dk, dv of every key through invariants that hold at any size (each row's
-    dS sums to zero over its keys, so dK sums to zero over all keys; each
-    row's P sums to one, so dV sums to the rows' dO)."""
+@pytest.mark.parametrize("name", ["c1", "c3", "c4"])
+def test_backward_full_size_sampled(torch_cuda, orc, name):
+    """Full-size workloads (the 64K-token zig-zag share, the 128K-token
+    documents share, the 1M-token GQA share) in the launch configuration the
+    benchmark times: dq on sampled rows against the oracle; dk, dv of every
+    key through invariants that hold at any size (each row's dS sums to zero
+    over its keys, so dK sums to zero over all keys of a KV head; each row's
+    P sums to one and every row sees at least its own key, so dV sums to the
+    rows' dO over the query heads of the KV head)."""
     from synth import WORKLOADS, bf16_bits_to_f32
-    wl = WORKLOADS["c1"]
-    say("backward c1 full size")
+    wl = WORKLOADS[name]
+    say("backward %s full size: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d,
+                                                                          wl.n_blocks))
     share, dout, dq, dk, dv = _run(torch_cuda, wl)
-    rows, heads = wl.sample_pairs(n_pairs=256)
+    rows, heads = wl.sample_pairs(n_pairs=128 if name == "c4" else 256)
     rdq, _, _ = oracle_grads(orc, wl, rows=rows, heads=heads)
-    grad_compare(dq.cpu().numpy()[rows, heads], rdq, "c1 dq (sampled)")
+    grad_compare(dq.cpu().numpy()[rows, heads], rdq, "%s dq (sampled)" % name)
     torch = torch_cuda
-    dk_all = torch.cat(dk).double()
-    dv_all = torch.cat(dv).double()
-    ksum = dk_all.sum(0)
-    kabs = dk_all.abs().sum(0)
+    group = wl.hq // wl.hkv
+    ksum = torch.zeros((wl.hkv, wl.d), dtype=torch.float64, device="cuda")
+    kabs = torch.zeros_like(ksum)
+    vsum = torch.zeros_like(ksum)
+    for b in range(wl.n_blocks):
+        x = dk[b].double()
+        ksum += x.sum(0)
+        kabs += x.abs().sum(0)
+        vsum += dv[b].double().sum(0)
     rel = float((ksum.abs() / kabs).max())
-    say("c1: max |sum_j dK_j| / sum_j |dK_j| = %.3e" % rel)
+    say("%s: max |sum_j dK_j| / sum_j |dK_j| = %.3e" % (name, rel))
     assert rel <= 1e-3
     do64 = torch.from_numpy(bf16_bits_to_f32(wl.dout()).astype(np.float64)).cuda()
-    vsum = dv_all.sum(0)                      # [hkv, d]
-    want = do64.sum(0)                         # every row sees at least its own key
+    want = do64.sum(0).reshape(wl.hkv, group, wl.d).sum(1)
     err = float((vsum - want).abs().max() / want.abs().max())
-    say("c1: max |sum_j dV_j - sum_i dO_i| / max = %.3e" % err)
+    say("%s: max |sum_j dV_j - sum_i dO_i| / max = %.3e" % (name, err))
     assert err <= 1e-3
+    del share, dq, dk, dv
+    torch.cuda.empty_cache()
 
 
 def test_backward_deterministic_and_accumulate(torch_cuda):
