@@ -19,11 +19,12 @@
 //  * Two kernels and no atomics. The key kernel: a workgroup of eight waves
 //    owns 128 keys of one KV head (32 per producer/consumer pair of waves)
 //    and walks the 32-row query tiles that can see them, for every query
-//    head that reads that KV head, accumulating dK and dV in registers. The query kernel: a workgroup owns
-//    128 rows (32 per wave) of one head and walks the 32-key tiles they can
-//    see, accumulating dQ. Both recompute S and dP (seven matrix products
-//    per visible pair instead of five) in exchange for no atomic traffic
-//    and run-to-run identical results.
+//    head that reads that KV head, accumulating dK and dV in registers. The
+//    query kernel: a workgroup of four waves owns 128 rows (32 per wave) of
+//    one head and walks the 32-key tiles they can see, accumulating dQ (two
+//    such workgroups share a CU). Both recompute S and dP (seven matrix
+//    products per visible pair instead of five) in exchange for no atomic
+//    traffic and run-to-run identical results.
 //  * Each wave keeps its own side's operands in registers for the whole
 //    call (K and V of its keys, or Q and dO of its rows) and streams the
 //    other side through LDS stages (four for the key kernel, two for the

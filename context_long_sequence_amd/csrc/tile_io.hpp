@@ -2,7 +2,8 @@
 // (partial_fwd.hip): tile geometry and LDS swizzles,
 // global -> LDS loads (direct and register-staged), the phase barrier and
 // register pins. NW is the number of waves that share one tile's loads.
-// Internal to the library.
+// The gradient kernels (partial_bwd.hip) use its buffer descriptors, scalar
+// clamp, workgroup remap and phase barrier. Internal to the library.
 #pragma once
 
 #include "device_common.hpp"
