@@ -92,6 +92,8 @@ def _reduced():
         "c2r": W["c2"].scaled(name="c2r", S=1024),
         "c3r": W["c3"].scaled(name="c3r", S=8192, hq=2, hkv=2, docs=(256, 2048)),
         "c4r": W["c4"].scaled(name="c4r", S=4096, hq=8, hkv=2),
+        # documents at d 64 with grouped KV heads
+        "c3r64": W["c3"].scaled(name="c3r64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
     }
 
 
@@ -106,7 +108,7 @@ def _run(torch, wl):
     return share, dout, dq, dk, dv
 
 
-@pytest.mark.parametrize("name", ["c0b", "c1r", "c2r", "c3r", "c4r"])
+@pytest.mark.parametrize("name", ["c0b", "c1r", "c2r", "c3r", "c4r", "c3r64"])
 def test_backward_reduced_all(torch_cuda, orc, name):
     wl = _reduced()[name]
     say("backward %s: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d, wl.n_blocks))

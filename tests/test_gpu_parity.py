@@ -96,10 +96,12 @@ def _reduced():
         "c2r": W["c2"].scaled(name="c2r", S=2048),
         "c3r": W["c3"].scaled(name="c3r", S=8192, hq=4, hkv=4, docs=(256, 2048)),
         "c4r": W["c4"].scaled(name="c4r", S=16384, hq=8, hkv=2),
+        # documents at d 64 with grouped KV heads
+        "c3r64": W["c3"].scaled(name="c3r64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
     }
 
 
-@pytest.mark.parametrize("name", ["c0", "c1r", "c2r", "c3r", "c4r"])
+@pytest.mark.parametrize("name", ["c0", "c1r", "c2r", "c3r", "c4r", "c3r64"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge"])
 def test_reduced_all_rows(torch_cuda, orc, name, mode):
     from context_long_sequence_amd.share import share_from_workload
@@ -111,6 +113,27 @@ def test_reduced_all_rows(torch_cuda, orc, name, mode):
     o, lse = to_np(o, lse)
     o_ref, lse_ref, _ = oracle_share(orc, wl)
     compare(o, lse, o_ref, lse_ref, None, None, O_TOL_F32 if wl.dtype == "f32" else O_TOL_BF16, name)
+
+
+@pytest.mark.parametrize("name", ["c1r", "c2r", "c3r", "c3r64"])
+@pytest.mark.parametrize("mode", ["accumulate", "merge", "fused"])
+def test_bf16_inputs_float32_output(torch_cuda, orc, name, mode):
+    """bf16 inputs with a float32 O: the float32 epilogue of the bf16 kernels
+    (d 64 and 128, with and without documents), per block with the merge in
+    the epilogue, per block with the standalone merge, and in one multi-block
+    call. The output is not rounded to bf16, so the bf16 bar holds with room."""
+    import torch
+    from context_long_sequence_amd.share import share_from_workload
+    wl = _reduced()[name]
+    say("%s float32 O, mode=%s" % (name, mode))
+    share = share_from_workload(wl)
+    share.o = torch.empty(share.o.shape, dtype=torch.float32, device="cuda")
+    o, lse = share.step(wl.arrival(), mode)
+    torch_cuda.cuda.synchronize()
+    assert o.dtype == torch.float32
+    o, lse = to_np(o, lse)
+    o_ref, lse_ref, _ = oracle_share(orc, wl)
+    compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, name + " float32 O")
 
 
 def test_per_block_partials(torch_cuda, orc):
