@@ -28,17 +28,18 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA pea
 
 
 KERNEL_SOURCES = ("partial_fwd.hip", "tile_io.hpp", "device_common.hpp", "kernels.hpp")
+BWD_KERNEL_SOURCES = ("partial_bwd.hip", "tile_io.hpp", "device_common.hpp", "kernels_bwd.hpp")
 
 
-def kernel_source_hash():
-    """sha256 over the partial-attention kernel's sources, in a fixed order,
-    with comments and blank lines removed (so that a comment edit does not
-    orphan a profile taken on the same code)."""
+def kernel_source_hash(sources=KERNEL_SOURCES):
+    """sha256 over a kernel's sources, in a fixed order, with comments and
+    blank lines removed (so that a comment edit does not orphan a profile
+    taken on the same code)."""
     import hashlib
     import re
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "context_long_sequence_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -48,19 +49,19 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def profiled_traffic(workload):
-    """HBM bytes per launch from a committed rocprofv3 counter summary under
-    profiles/, or None when no summary was taken on the current kernel sources
-    for this workload."""
+def profiled_traffic(workload, sources=KERNEL_SOURCES, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch (or per `key`) from a committed rocprofv3 counter
+    summary under profiles/, or None when no summary was taken on the current
+    kernel sources for this workload."""
     import glob
     import re
-    want = kernel_source_hash()
+    want = kernel_source_hash(sources)
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
     for path in sorted(glob.glob(os.path.join(root, "*.md"))):
         text = open(path).read()
         src = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", text, re.M)
         wl = re.search(r"^workload: (\S+)$", text, re.M)
-        tr = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+        tr = re.search(r"^%s: (\d+)$" % key, text, re.M)
         if src and wl and tr and src.group(1) == want and wl.group(1) == workload:
             return int(tr.group(1))
     return None
@@ -144,7 +145,8 @@ def main():
         fused_step(wl, share, order, step_flops, args.steps, args.warmup)
         return
     if args.backward:
-        backward_step(wl, share, order, step_flops, args.steps, args.warmup)
+        backward_step(wl, share, order, step_flops, args.steps, args.warmup,
+                      None if args.no_cpu_baseline else args.cpu_seconds)
         return
 
     for _ in range(args.warmup):
@@ -253,25 +255,33 @@ def fused_step(wl, share, order, step_flops, steps, warmup):
                       "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
 
 
-def backward_step(wl, share, order, step_flops, steps, warmup):
+def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None):
     """The gradient step of the share, timed: one cpattn_bwd_delta call, then
     one cpattn_partial_bwd call per block (its key kernel and query kernel).
     Algorithmic work is five matrix products per visible pair (S, dP, dV, dK,
     dQ: 2.5 times the forward's two); the kernels run seven (S and dP are
-    formed in both kernels). Prints one JSON line."""
+    formed in both kernels). The step time comes from a region with events at
+    its ends only; the mean block-call duration for the roofline from a second
+    pass with an event pair around every call. Prints one JSON line."""
     import torch
     from context_long_sequence_amd.share import bits_to_device
     from context_long_sequence_amd import cpattn_bwd_delta, cpattn_partial_bwd
     share.step(order)
-    dout = bits_to_device(wl.dout())
+    dout_host = wl.dout()
+    dout = bits_to_device(dout_host)
     for _ in range(max(1, warmup)):   # (the first call also allocates the gradient buffers)
         share.backward(dout, order)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    n_launch = steps * len(order)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    for _ in range(steps):
+        share.backward(dout, order)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    n_call = steps * len(order)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_call)]
     n = 0
     for _ in range(steps):
         cpattn_bwd_delta(share.o, dout, share.delta)
@@ -282,20 +292,36 @@ def backward_step(wl, share, order, step_flops, steps, warmup):
                                causal=share.causal, accumulate_dq=i > 0, cu_seqlens=share.cu_seqlens)
             ev[2 * n + 1].record(stream)
             n += 1
-    stop.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
-    call_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_launch)]))
+    call_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_call)]))
     bwd_flops = 2.5 * step_flops
     tflops = bwd_flops / (ms * 1e-3) / 1e12
+    call_flops = bwd_flops / len(order)
+    achieved = call_flops / (call_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
     log("backward step: %.3f ms/step, %.1f TFLOP/s algorithmic (%.1f executed), %.3f ms per block call" %
         (ms, tflops, tflops * 1.4, call_ms))
-    print(json.dumps({"metric": "causal-effective backward TFLOP/s of one rank share (bf16 MFMA, fp32 gradients)",
-                      "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
-                      "warmup": warmup, "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
-                      "algorithmic_flop_per_step": bwd_flops, "executed_flop_per_step": 1.4 * bwd_flops,
-                      "mean_block_call_ms": round(call_ms, 5),
-                      "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
+    out = {"metric": "causal-effective backward TFLOP/s of one rank share (bf16 MFMA, fp32 gradients)",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
+           "warmup": warmup, "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
+           "algorithmic_flop_per_step": bwd_flops, "executed_flop_per_step": 1.4 * bwd_flops,
+           "mean_block_call_ms": round(call_ms, 5),
+           "pct_of_peak": round(100.0 * tflops / peak, 2),
+           "roofline": {
+               "kernel": "one block's backward call: bwd_dkv_kernel then bwd_dq_kernel",
+               "bound": "mfma",
+               "achieved": round(achieved, 2),
+               "peak": peak,
+               "unit": "TFLOP/s",
+               "frac": round(achieved / peak, 4),
+               "traffic": profiled_traffic(wl.name, BWD_KERNEL_SOURCES, "traffic_bytes_per_block_call"),
+               "flop_per_call": call_flops,
+               "mean_call_ms": round(call_ms, 5),
+               "calls": n_call,
+           }}
+    if cpu_seconds:
+        out["cpu_baseline"] = cpu_baseline_bwd(wl, share, dout_host, cpu_seconds)
+    print(json.dumps(out), flush=True)
 
 
 def pipeline_sweep(wl, share, order, step_flops, chunks=(1024, 2048, 4096, 8192), slots=3, reps=3):
@@ -385,6 +411,64 @@ def cpu_baseline(wl, share, seconds):
                   "softmax attention, %.1f s" % (len(rows), dt),
         "seconds": round(dt, 3),
         "gpu_vs_oracle_max_abs_err": {"o": eo, "lse": el},
+    }
+
+
+def cpu_baseline_bwd(wl, share, dout_host, seconds):
+    """Time the fp64 oracle's gradients on a bounded sample of the workload's
+    rows (dQ of sampled (row, head) pairs against all keys: the oracle forms
+    scores, O for D, dP and dQ, four products per visible pair), and check the
+    GPU's dQ on that sample."""
+    import oracle
+    from synth import bf16_bits_to_f32
+    orc = oracle.get()
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    docs = wl.doc_lens()
+    qp, qst = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
+    kps = []
+    for b in range(wl.n_blocks):
+        if wl.block_kind == "rank_shares":
+            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
+        elif wl.block_kind == "chunks":
+            c = wl.S // wl.n_blocks
+            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
+        else:
+            kps.append(np.arange(wl.S, dtype=np.int32))
+    log("cpu baseline (backward): loading inputs on the host")
+    q = wl.q()
+    k = np.concatenate([wl.kv_block(b, "k") for b in range(wl.n_blocks)])
+    v = np.concatenate([wl.kv_block(b, "v") for b in range(wl.n_blocks)])
+    dout = bf16_bits_to_f32(dout_host).astype(np.float64)
+    kp = np.concatenate(kps)
+    qstart = qst if docs is not None else None
+    n = 16
+    while True:
+        rows, heads = wl.sample_pairs(n)
+        t = time.perf_counter()
+        dq_ref, _, _, _ = orc.attention_grad(q, k, v, dout, qp, kp, qstart, True, rows=rows, heads=heads,
+                                             n_threads=threads)
+        dt = time.perf_counter() - t
+        if dt >= 0.5 * seconds or n >= wl.lq * wl.hq:
+            break
+        n = int(min(wl.lq * wl.hq, max(2 * n, n * seconds / max(dt, 1e-3))))
+    kp_sorted = np.sort(kp)   # (the blocks' keys, concatenated, need not ascend)
+    hi = np.searchsorted(kp_sorted, qp[rows], side="right")
+    lo = 0 if qstart is None else np.searchsorted(kp_sorted, qstart[rows], side="left")
+    pairs = float(np.sum(hi - lo))
+    flops = 8.0 * wl.d * pairs
+    dq = share.dq.cpu().numpy()[rows, heads]
+    rel = float(np.max(np.abs(dq - dq_ref)) / max(np.max(np.abs(dq_ref)), 1e-30))
+    log("cpu baseline (backward): %d (row, head) pairs in %.1f s on %d threads; GPU vs oracle max|ddQ|/max|dQ| %.2e"
+        % (len(rows), dt, threads, rel))
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "dQ of %d sampled (query row, head) pairs of this workload against all its keys, fp64, "
+                  "8 d flop per visible pair (scores, O, dP, dQ), %.1f s" % (len(rows), dt),
+        "seconds": round(dt, 3),
+        "gpu_vs_oracle_dq_max_rel_err": rel,
     }
 
 
