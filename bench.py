@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="instead of the headline line, time the step as ONE cpattn_partial_multi call over all "
                          "blocks (state kept in registers between blocks); one JSON line")
+    ap.add_argument("--merge", action="store_true",
+                    help="instead of the headline line, time the standalone LSE merge kernel on the workload's "
+                         "(O, LSE) shape against the HBM roofline; one JSON line")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the headline line, time the gradient step on the workload: D = <dO, O> "
                          "once, then the backward of every KV block in arrival order (dQ summed over blocks, "
@@ -123,6 +126,9 @@ def main():
         return
     cp.load_library()  # fails loudly if the HIP library is missing
     wl = WORKLOADS[args.workload]
+    if args.merge:
+        merge_bench(wl, args.steps, args.warmup)
+        return
     log("workload %s: %s" % (wl.name, wl.description))
     t0 = time.time()
     share = share_from_workload(wl)
@@ -253,6 +259,45 @@ def fused_step(wl, share, order, step_flops, steps, warmup):
                       "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
                       "higher_is_better": True, "workload": wl.name, "kv_blocks": len(order),
                       "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[wl.dtype], 2)}), flush=True)
+
+
+def merge_bench(wl, steps, warmup, reps=10):
+    """The standalone merge (o_acc, lse_acc) <- merge(acc, part) on the
+    workload's output shape: algorithmic bytes per launch = O_acc and O_part
+    read, O_acc written, two LSEs read and one written. Timed with one event
+    pair around each launch on the launch stream; one JSON line with the HBM
+    roofline."""
+    import torch
+    from context_long_sequence_amd import cpattn_merge_lse
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(7)
+    shape = (wl.lq, wl.hq, wl.d)
+    o_acc = torch.randn(shape, generator=g, device="cuda").to(dt)
+    o_part = torch.randn(shape, generator=g, device="cuda").to(dt)
+    lse_acc = torch.rand((wl.hq, wl.lq), generator=g, device="cuda") * 10
+    lse_part = torch.rand((wl.hq, wl.lq), generator=g, device="cuda") * 10
+    for _ in range(warmup):
+        cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n = steps * reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        ev[2 * i].record(stream)
+        cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]))
+    esz = 2 if dt == torch.bfloat16 else 4
+    rows = wl.lq * wl.hq
+    nbytes = 3 * rows * wl.d * esz + 3 * rows * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("merge: %.4f ms per launch, %.1f GB/s (%.1f MB per launch)" % (ms, gbs, nbytes / 1e6))
+    print(json.dumps({"metric": "standalone LSE merge: HBM throughput", "value": round(gbs, 1), "unit": "GB/s",
+                      "higher_is_better": True, "workload": wl.name, "launches": n, "mean_launch_ms": round(ms, 5),
+                      "roofline": {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
+                                   "traffic": None, "bytes_per_launch": nbytes}}), flush=True)
 
 
 def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None):
