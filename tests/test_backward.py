@@ -184,7 +184,7 @@ def _rand_bf16(torch, shape, seed):
 
 def _ragged_cases():
     out = []
-    for lq, lk, hq, hkv in [(100, 77, 2, 1), (257, 300, 3, 3), (33, 1, 4, 2)]:
+    for lq, lk, hq, hkv in [(100, 77, 2, 1), (257, 300, 3, 3), (33, 1, 4, 2), (70, 130, 16, 1), (50, 40, 3, 1)]:
         for causal in (True, False):
             for d in (64, 128):
                 marks = ()

@@ -319,9 +319,12 @@ def _rand_dev(shape, seed, dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("lq,lk,hq,hkv", [(300, 200, 6, 3), (1, 77, 2, 2), (33, 65, 4, 1), (129, 1000, 8, 8)])
+@pytest.mark.parametrize("lq,lk,hq,hkv", [(300, 200, 6, 3), (1, 77, 2, 2), (33, 65, 4, 1), (129, 1000, 8, 8),
+                                         (50, 40, 3, 1), (70, 130, 16, 1)])
 def test_ragged_random_positions(torch_cuda, orc, d, dtype, lq, lk, hq, hkv):
-    """Sizes that are not multiples of any tile, arbitrary ascending positions."""
+    """Sizes that are not multiples of any tile, arbitrary ascending positions;
+    query-head groups of 1, 2, 3 (not packable), 4 and 16 (8 heads per
+    workgroup, two workgroups per group)."""
     import torch
     from synth import normal_tensor
     from context_long_sequence_amd import cpattn_partial
