@@ -109,7 +109,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of this build "
+        print("bench.py measures one GPU's rank share only; runs on more than one GPU are not supported "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
