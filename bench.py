@@ -86,7 +86,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c1", help="c0..c4 (default c1, the headline configuration)")
+    ap.add_argument("--workload", default="zigzag64k_cp8_h32_d128", help="one of synth.WORKLOADS (default: the 64K-token zig-zag cp 8 rank share)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

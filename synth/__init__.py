@@ -169,23 +169,23 @@ class Workload:
 
 
 WORKLOADS = {
-    "c0": Workload("c0", S=1024, cp=4, rank=1, layout="zigzag", hq=1, hkv=1, d=64, dtype="f32", sigma=1.0,
+    "zigzag1k_cp4_h1_d64_f32": Workload("zigzag1k_cp4_h1_d64_f32", S=1024, cp=4, rank=1, layout="zigzag", hq=1, hkv=1, d=64, dtype="f32", sigma=1.0,
                    block_kind="rank_shares", n_blocks=4, seed=1000,
                    description="1 head, d64, fp32, 1024 tokens zig-zag cp4, rank 1: 256 queries vs 4 rank-share "
                                "blocks of 256 in seeded order"),
-    "c1": Workload("c1", S=65536, cp=8, rank=1, layout="zigzag", hq=32, hkv=32, d=128, dtype="bf16", sigma=0.5,
+    "zigzag64k_cp8_h32_d128": Workload("zigzag64k_cp8_h32_d128", S=65536, cp=8, rank=1, layout="zigzag", hq=32, hkv=32, d=128, dtype="bf16", sigma=0.5,
                    block_kind="rank_shares", n_blocks=8, seed=1001,
                    description="7B-class layer, 64K tokens zig-zag cp8, rank 1: 8192 queries x 32 heads, d128, "
                                "vs 8 rank-share blocks of 8192 in seeded order"),
-    "c2": Workload("c2", S=131072, cp=1, rank=0, layout="contiguous", hq=16, hkv=2, d=64, dtype="bf16", sigma=1.0,
+    "contig128k_h16kv2_d64": Workload("contig128k_h16kv2_d64", S=131072, cp=1, rank=0, layout="contiguous", hq=16, hkv=2, d=64, dtype="bf16", sigma=1.0,
                    block_kind="whole", n_blocks=1, seed=1002, sampled_rows=4096,
                    description="Ulysses head share of cp4 with 64 Q / 8 KV heads: 16 Q / 2 KV heads, d64, full "
                                "causal 131072 tokens"),
-    "c3": Workload("c3", S=131072, cp=4, rank=1, layout="zigzag", hq=32, hkv=32, d=128, dtype="bf16", sigma=0.5,
+    "docs128k_zigzag_cp4_h32_d128": Workload("docs128k_zigzag_cp4_h32_d128", S=131072, cp=4, rank=1, layout="zigzag", hq=32, hkv=32, d=128, dtype="bf16", sigma=0.5,
                    block_kind="rank_shares", n_blocks=4, seed=1003, docs=(1024, 32768),
                    description="packed 128K tokens of log-uniform [1K,32K] documents, per-document zig-zag cp4, "
                                "rank 1: 32768 queries x 32 heads, d128, vs 4 rank-share blocks"),
-    "c4": Workload("c4", S=1 << 20, cp=8, rank=1, layout="zigzag", hq=32, hkv=8, d=128, dtype="bf16", sigma=0.5,
+    "zigzag1m_cp8_h32kv8_d128": Workload("zigzag1m_cp8_h32kv8_d128", S=1 << 20, cp=8, rank=1, layout="zigzag", hq=32, hkv=8, d=128, dtype="bf16", sigma=0.5,
                    block_kind="chunks", n_blocks=16, seed=1004, sampled_rows=2048,
                    description="1M tokens zig-zag cp8, rank 1: 131072 queries x 32 Q / 8 KV heads, d128, vs 16 "
                                "chunks of 65536 in seeded order"),

@@ -87,13 +87,13 @@ def oracle_grads(orc, wl, rows=None, heads=None):
 def _reduced():
     from synth import WORKLOADS as W
     return {
-        "c0b": W["c0"].scaled(name="c0b", dtype="bf16"),
-        "c1r": W["c1"].scaled(name="c1r", S=4096, hq=4, hkv=4),
-        "c2r": W["c2"].scaled(name="c2r", S=1024),
-        "c3r": W["c3"].scaled(name="c3r", S=8192, hq=2, hkv=2, docs=(256, 2048)),
-        "c4r": W["c4"].scaled(name="c4r", S=4096, hq=8, hkv=2),
+        "zigzag1k_cp4_h1_d64_bf16": W["zigzag1k_cp4_h1_d64_f32"].scaled(name="zigzag1k_cp4_h1_d64_bf16", dtype="bf16"),
+        "zigzag4k_cp8_h4_d128": W["zigzag64k_cp8_h32_d128"].scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
+        "contig1k_h16kv2_d64": W["contig128k_h16kv2_d64"].scaled(name="contig1k_h16kv2_d64", S=1024),
+        "docs8k_zigzag_cp4_h2_d128": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h2_d128", S=8192, hq=2, hkv=2, docs=(256, 2048)),
+        "zigzag4k_cp8_h8kv2_d128": W["zigzag1m_cp8_h32kv8_d128"].scaled(name="zigzag4k_cp8_h8kv2_d128", S=4096, hq=8, hkv=2),
         # documents at d 64 with grouped KV heads
-        "c3r64": W["c3"].scaled(name="c3r64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
+        "docs8k_zigzag_cp4_h4kv2_d64": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
     }
 
 
@@ -108,7 +108,7 @@ def _run(torch, wl):
     return share, dout, dq, dk, dv
 
 
-@pytest.mark.parametrize("name", ["c0b", "c1r", "c2r", "c3r", "c4r", "c3r64"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_bf16", "zigzag4k_cp8_h4_d128", "contig1k_h16kv2_d64", "docs8k_zigzag_cp4_h2_d128", "zigzag4k_cp8_h8kv2_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
 def test_backward_reduced_all(torch_cuda, orc, name):
     wl = _reduced()[name]
     say("backward %s: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d, wl.n_blocks))
@@ -120,12 +120,12 @@ def test_backward_reduced_all(torch_cuda, orc, name):
 
 
 def _large(name):
-    """A full-size workload, or c3h: the documents workload at half its length
+    """A full-size workload, or the documents workload at half its length
     (65536 packed tokens of log-uniform [1K, 32K] documents, per-document
     zig-zag cp 4, rank 1: 16384 queries x 32 heads, d 128, vs 4 blocks)."""
     from synth import WORKLOADS
-    if name == "c3h":
-        return WORKLOADS["c3"].scaled(name="c3h", S=65536)
+    if name == "docs64k_zigzag_cp4_h32_d128":
+        return WORKLOADS["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs64k_zigzag_cp4_h32_d128", S=65536)
     return WORKLOADS[name]
 
 
@@ -134,11 +134,11 @@ def _large(name):
 # cause was shown, and the case stays off the GPU until one is. (The full-size
 # documents forward is still compared with the oracle by the forward parity
 # tests, and the documents backward at half length here and at reduced sizes.)
-@pytest.mark.parametrize("name", ["c1",
-                                  pytest.param("c3", marks=pytest.mark.skip(
+@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128",
+                                  pytest.param("docs128k_zigzag_cp4_h32_d128", marks=pytest.mark.skip(
                                       reason="faulted the GPU with an earlier forward-kernel variant; "
                                              "cause not yet shown")),
-                                  "c3h", "c4"])
+                                  "docs64k_zigzag_cp4_h32_d128", "zigzag1m_cp8_h32kv8_d128"])
 def test_backward_full_size_sampled(torch_cuda, orc, name):
     """Full-size workloads (the 64K-token zig-zag share, the 128K-token
     documents share, the 1M-token GQA share) in the launch configuration the
@@ -152,7 +152,7 @@ def test_backward_full_size_sampled(torch_cuda, orc, name):
     say("backward %s full size: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d,
                                                                           wl.n_blocks))
     share, dout, dq, dk, dv = _run(torch_cuda, wl)
-    rows, heads = wl.sample_pairs(n_pairs=128 if name == "c4" else 256)
+    rows, heads = wl.sample_pairs(n_pairs=128 if name == "zigzag1m_cp8_h32kv8_d128" else 256)
     rdq, _, _ = oracle_grads(orc, wl, rows=rows, heads=heads)
     grad_compare(dq.cpu().numpy()[rows, heads], rdq, "%s dq (sampled)" % name)
     torch = torch_cuda
@@ -178,7 +178,7 @@ def test_backward_full_size_sampled(torch_cuda, orc, name):
 
 
 def test_backward_deterministic_and_accumulate(torch_cuda):
-    wl = _reduced()["c4r"]
+    wl = _reduced()["zigzag4k_cp8_h8kv2_d128"]
     torch = torch_cuda
     from context_long_sequence_amd import cpattn_partial_bwd
     share, dout, dq, dk, dv = _run(torch, wl)

@@ -91,17 +91,17 @@ def compare(o, lse, o_ref, lse_ref, rows, heads, o_tol, what, lse_tol=LSE_TOL):
 def _reduced():
     from synth import WORKLOADS as W
     return {
-        "c0": W["c0"],
-        "c1r": W["c1"].scaled(name="c1r", S=4096, hq=4, hkv=4),
-        "c2r": W["c2"].scaled(name="c2r", S=2048),
-        "c3r": W["c3"].scaled(name="c3r", S=8192, hq=4, hkv=4, docs=(256, 2048)),
-        "c4r": W["c4"].scaled(name="c4r", S=16384, hq=8, hkv=2),
+        "zigzag1k_cp4_h1_d64_f32": W["zigzag1k_cp4_h1_d64_f32"],
+        "zigzag4k_cp8_h4_d128": W["zigzag64k_cp8_h32_d128"].scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
+        "contig2k_h16kv2_d64": W["contig128k_h16kv2_d64"].scaled(name="contig2k_h16kv2_d64", S=2048),
+        "docs8k_zigzag_cp4_h4_d128": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4_d128", S=8192, hq=4, hkv=4, docs=(256, 2048)),
+        "zigzag16k_cp8_h8kv2_d128": W["zigzag1m_cp8_h32kv8_d128"].scaled(name="zigzag16k_cp8_h8kv2_d128", S=16384, hq=8, hkv=2),
         # documents at d 64 with grouped KV heads
-        "c3r64": W["c3"].scaled(name="c3r64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
+        "docs8k_zigzag_cp4_h4kv2_d64": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
     }
 
 
-@pytest.mark.parametrize("name", ["c0", "c1r", "c2r", "c3r", "c4r", "c3r64"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge"])
 def test_reduced_all_rows(torch_cuda, orc, name, mode):
     from context_long_sequence_amd.share import share_from_workload
@@ -115,7 +115,7 @@ def test_reduced_all_rows(torch_cuda, orc, name, mode):
     compare(o, lse, o_ref, lse_ref, None, None, O_TOL_F32 if wl.dtype == "f32" else O_TOL_BF16, name)
 
 
-@pytest.mark.parametrize("name", ["c1r", "c2r", "c3r", "c3r64"])
+@pytest.mark.parametrize("name", ["zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge", "fused"])
 def test_bf16_inputs_float32_output(torch_cuda, orc, name, mode):
     """bf16 inputs with a float32 O: the float32 epilogue of the bf16 kernels
@@ -139,7 +139,7 @@ def test_bf16_inputs_float32_output(torch_cuda, orc, name, mode):
 def test_per_block_partials(torch_cuda, orc):
     """Each block alone (accumulate = 0), including rows that see nothing in it."""
     from context_long_sequence_amd.share import share_from_workload
-    for name in ("c0", "c1r", "c4r"):
+    for name in ("zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "zigzag16k_cp8_h8kv2_d128"):
         wl = _reduced()[name]
         share = share_from_workload(wl)
         for b in range(wl.n_blocks):
@@ -158,7 +158,7 @@ def test_accumulate_leaves_unseeing_rows_bit_identical(torch_cuda):
     At the reduced 64K-share shape whole workgroups see nothing of most blocks
     and return early; the rest see it partly or wholly."""
     from context_long_sequence_amd.share import share_from_workload
-    wl = _reduced()["c1r"]
+    wl = _reduced()["zigzag4k_cp8_h4_d128"]
     share = share_from_workload(wl)
     order = list(wl.arrival())
     share.call_block(order[0], share.o, share.lse, accumulate=False)
@@ -178,10 +178,10 @@ def test_accumulate_leaves_unseeing_rows_bit_identical(torch_cuda):
     assert n_checked > 0
 
 
-FULL_SAMPLES = {"c1": 512, "c2": 1024, "c3": 512, "c4": 128}
+FULL_SAMPLES = {"zigzag64k_cp8_h32_d128": 512, "contig128k_h16kv2_d64": 1024, "docs128k_zigzag_cp4_h32_d128": 512, "zigzag1m_cp8_h32kv8_d128": 128}
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128", "contig128k_h16kv2_d64", "docs128k_zigzag_cp4_h32_d128", "zigzag1m_cp8_h32kv8_d128"])
 def test_full_size_sampled(torch_cuda, orc, name):
     from context_long_sequence_amd.share import share_from_workload
     from synth import WORKLOADS
@@ -206,7 +206,7 @@ def _visible_counts(q_pos, k_pos_all, q_start=None):
     return hi - lo, lo, hi
 
 
-@pytest.mark.parametrize("name", ["c1", "c3"])
+@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128", "docs128k_zigzag_cp4_h32_d128"])
 def test_full_size_zero_q_closed_form(torch_cuda, name):
     """Q = 0 gives uniform weights: LSE = ln(#visible) for EVERY row, and O the
     mean of the visible values (checked on sampled rows from host prefix sums)."""
@@ -246,17 +246,17 @@ def test_full_size_zero_q_closed_form(torch_cuda, name):
 
 def test_order_independence_and_determinism(torch_cuda, orc):
     from context_long_sequence_amd.share import share_from_workload
-    wl = _reduced()["c1r"]
+    wl = _reduced()["zigzag4k_cp8_h4_d128"]
     share = share_from_workload(wl)
     outs = []
     for order in ([0, 1, 2, 3, 4, 5, 6, 7], [7, 6, 5, 4, 3, 2, 1, 0], list(wl.arrival()), [3, 0, 7, 1, 6, 2, 5, 4]):
-        say("c1r order %s" % order)
+        say("%s order %s" % (wl.name, order))
         o, lse = share.step(order, "accumulate")
         torch_cuda.cuda.synchronize()
         outs.append(to_np(o, lse))
     o_ref, lse_ref, _ = oracle_share(orc, wl)
     for o, lse in outs:
-        compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, "c1r any order")
+        compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, wl.name + " any order")
     for o, lse in outs[1:]:
         assert np.max(np.abs(o - outs[0][0])) <= 2 ** -7
         assert np.max(np.abs(lse - outs[0][1])) <= 4e-6
@@ -267,7 +267,7 @@ def test_order_independence_and_determinism(torch_cuda, orc):
 def test_gqa_equals_repeated_kv(torch_cuda):
     """Grouped KV heads give the same result as KV heads copied per query head."""
     from context_long_sequence_amd.share import RankShare, share_from_workload
-    wl = _reduced()["c4r"]
+    wl = _reduced()["zigzag16k_cp8_h8kv2_d128"]
     gqa = share_from_workload(wl)
     G = wl.hq // wl.hkv
     rep = RankShare(gqa.q, [k.repeat_interleave(G, dim=1).contiguous() for k in gqa.k_blocks],
@@ -286,7 +286,7 @@ def test_late_block_with_much_larger_scores(torch_cuda, orc):
     import torch
     from context_long_sequence_amd.share import share_from_workload
     from synth import f32_to_bf16_bits, bf16_bits_to_f32
-    wl = _reduced()["c1r"]
+    wl = _reduced()["zigzag4k_cp8_h4_d128"]
     share = share_from_workload(wl)
     order = list(wl.arrival())
     late = order[-1]

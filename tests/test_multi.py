@@ -22,7 +22,7 @@ def orc():
     return oracle.get()
 
 
-@pytest.mark.parametrize("name", ["c0", "c1r", "c2r", "c3r", "c4r"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128"])
 def test_fused_all_rows(torch_cuda, orc, name):
     from context_long_sequence_amd.share import share_from_workload
     from test_gpu_parity import O_TOL_BF16, O_TOL_F32, _reduced, compare, oracle_share, say, to_np
@@ -40,7 +40,7 @@ def test_fused_one_block_equals_single_block_call(torch_cuda):
     """One block through the multi-block kernel is the single-block call, bit for bit."""
     from context_long_sequence_amd.share import share_from_workload
     from test_gpu_parity import _reduced
-    for name in ("c1r", "c3r", "c4r"):
+    for name in ("zigzag4k_cp8_h4_d128", "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128"):
         wl = _reduced()[name]
         share = share_from_workload(wl)
         for b in range(wl.n_blocks):
@@ -61,7 +61,7 @@ def test_fused_accumulate_and_split_order(torch_cuda, orc):
     another order: the union of all blocks."""
     from context_long_sequence_amd.share import share_from_workload
     from test_gpu_parity import O_TOL_BF16, _reduced, compare, oracle_share, to_np
-    wl = _reduced()["c1r"]
+    wl = _reduced()["zigzag4k_cp8_h4_d128"]
     share = share_from_workload(wl)
     order = list(wl.arrival())[::-1]
     share.call_multi(order[:3], share.o, share.lse, accumulate=False)
@@ -69,7 +69,7 @@ def test_fused_accumulate_and_split_order(torch_cuda, orc):
     torch_cuda.cuda.synchronize()
     o, lse = to_np(share.o, share.lse)
     o_ref, lse_ref, _ = oracle_share(orc, wl)
-    compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, "c1r fused 3 + 5")
+    compare(o, lse, o_ref, lse_ref, None, None, O_TOL_BF16, wl.name + " fused 3 + 5")
 
 
 def test_fused_with_empty_and_invisible_blocks(torch_cuda):
@@ -103,7 +103,7 @@ def test_fused_with_empty_and_invisible_blocks(torch_cuda):
     assert torch.equal(o, o0) and torch.equal(lse, l0)
 
 
-@pytest.mark.parametrize("name", ["c1", "c4"])
+@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128", "zigzag1m_cp8_h32kv8_d128"])
 def test_fused_full_size_sampled(torch_cuda, orc, name):
     from context_long_sequence_amd.share import share_from_workload
     from synth import WORKLOADS

@@ -66,7 +66,7 @@ def test_pipeline_matches_unpipelined_and_oracle(source, chunk, slots):
     from context_long_sequence_amd.pipeline import ArrivalPipeline
     from context_long_sequence_amd.share import share_from_workload
     from test_gpu_parity import O_TOL_BF16, _reduced, compare, oracle_share, say, to_np
-    wl = _reduced()["c1r"]
+    wl = _reduced()["zigzag4k_cp8_h4_d128"]
     share = share_from_workload(wl)
     order = list(wl.arrival())
     pipe = ArrivalPipeline(share, chunk, n_slots=slots, source=source)
