@@ -86,15 +86,18 @@ def oracle_grads(orc, wl, rows=None, heads=None):
 
 def _reduced():
     from synth import WORKLOADS as W
-    return {
-        "zigzag1k_cp4_h1_d64_bf16": W["zigzag1k_cp4_h1_d64_f32"].scaled(name="zigzag1k_cp4_h1_d64_bf16", dtype="bf16"),
-        "zigzag4k_cp8_h4_d128": W["zigzag64k_cp8_h32_d128"].scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
-        "contig1k_h16kv2_d64": W["contig128k_h16kv2_d64"].scaled(name="contig1k_h16kv2_d64", S=1024),
-        "docs8k_zigzag_cp4_h2_d128": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h2_d128", S=8192, hq=2, hkv=2, docs=(256, 2048)),
-        "zigzag4k_cp8_h8kv2_d128": W["zigzag1m_cp8_h32kv8_d128"].scaled(name="zigzag4k_cp8_h8kv2_d128", S=4096, hq=8, hkv=2),
+    zz64k, contig, docs, zz1m = (W["zigzag64k_cp8_h32_d128"], W["contig128k_h16kv2_d64"],
+                                 W["docs128k_zigzag_cp4_h32_d128"], W["zigzag1m_cp8_h32kv8_d128"])
+    wls = [
+        W["zigzag1k_cp4_h1_d64_f32"].scaled(name="zigzag1k_cp4_h1_d64_bf16", dtype="bf16"),
+        zz64k.scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
+        contig.scaled(name="contig1k_h16kv2_d64", S=1024),
+        docs.scaled(name="docs8k_zigzag_cp4_h2_d128", S=8192, hq=2, hkv=2, docs=(256, 2048)),
+        zz1m.scaled(name="zigzag4k_cp8_h8kv2_d128", S=4096, hq=8, hkv=2),
         # documents at d 64 with grouped KV heads
-        "docs8k_zigzag_cp4_h4kv2_d64": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
-    }
+        docs.scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
+    ]
+    return {w.name: w for w in wls}
 
 
 def _run(torch, wl):
@@ -108,7 +111,9 @@ def _run(torch, wl):
     return share, dout, dq, dk, dv
 
 
-@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_bf16", "zigzag4k_cp8_h4_d128", "contig1k_h16kv2_d64", "docs8k_zigzag_cp4_h2_d128", "zigzag4k_cp8_h8kv2_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_bf16", "zigzag4k_cp8_h4_d128", "contig1k_h16kv2_d64",
+                                  "docs8k_zigzag_cp4_h2_d128", "zigzag4k_cp8_h8kv2_d128",
+                                  "docs8k_zigzag_cp4_h4kv2_d64"])
 def test_backward_reduced_all(torch_cuda, orc, name):
     wl = _reduced()[name]
     say("backward %s: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d, wl.n_blocks))

@@ -90,18 +90,23 @@ def compare(o, lse, o_ref, lse_ref, rows, heads, o_tol, what, lse_tol=LSE_TOL):
 
 def _reduced():
     from synth import WORKLOADS as W
-    return {
-        "zigzag1k_cp4_h1_d64_f32": W["zigzag1k_cp4_h1_d64_f32"],
-        "zigzag4k_cp8_h4_d128": W["zigzag64k_cp8_h32_d128"].scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
-        "contig2k_h16kv2_d64": W["contig128k_h16kv2_d64"].scaled(name="contig2k_h16kv2_d64", S=2048),
-        "docs8k_zigzag_cp4_h4_d128": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4_d128", S=8192, hq=4, hkv=4, docs=(256, 2048)),
-        "zigzag16k_cp8_h8kv2_d128": W["zigzag1m_cp8_h32kv8_d128"].scaled(name="zigzag16k_cp8_h8kv2_d128", S=16384, hq=8, hkv=2),
+    zz64k, contig, docs, zz1m = (W["zigzag64k_cp8_h32_d128"], W["contig128k_h16kv2_d64"],
+                                 W["docs128k_zigzag_cp4_h32_d128"], W["zigzag1m_cp8_h32kv8_d128"])
+    wls = [
+        W["zigzag1k_cp4_h1_d64_f32"],
+        zz64k.scaled(name="zigzag4k_cp8_h4_d128", S=4096, hq=4, hkv=4),
+        contig.scaled(name="contig2k_h16kv2_d64", S=2048),
+        docs.scaled(name="docs8k_zigzag_cp4_h4_d128", S=8192, hq=4, hkv=4, docs=(256, 2048)),
+        zz1m.scaled(name="zigzag16k_cp8_h8kv2_d128", S=16384, hq=8, hkv=2),
         # documents at d 64 with grouped KV heads
-        "docs8k_zigzag_cp4_h4kv2_d64": W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
-    }
+        docs.scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
+    ]
+    return {w.name: w for w in wls}
 
 
-@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64",
+                                  "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128",
+                                  "docs8k_zigzag_cp4_h4kv2_d64"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge"])
 def test_reduced_all_rows(torch_cuda, orc, name, mode):
     from context_long_sequence_amd.share import share_from_workload
@@ -115,7 +120,8 @@ def test_reduced_all_rows(torch_cuda, orc, name, mode):
     compare(o, lse, o_ref, lse_ref, None, None, O_TOL_F32 if wl.dtype == "f32" else O_TOL_BF16, name)
 
 
-@pytest.mark.parametrize("name", ["zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
+@pytest.mark.parametrize("name", ["zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128",
+                                  "docs8k_zigzag_cp4_h4kv2_d64"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge", "fused"])
 def test_bf16_inputs_float32_output(torch_cuda, orc, name, mode):
     """bf16 inputs with a float32 O: the float32 epilogue of the bf16 kernels
@@ -178,10 +184,11 @@ def test_accumulate_leaves_unseeing_rows_bit_identical(torch_cuda):
     assert n_checked > 0
 
 
-FULL_SAMPLES = {"zigzag64k_cp8_h32_d128": 512, "contig128k_h16kv2_d64": 1024, "docs128k_zigzag_cp4_h32_d128": 512, "zigzag1m_cp8_h32kv8_d128": 128}
+FULL_SAMPLES = {"zigzag64k_cp8_h32_d128": 512, "contig128k_h16kv2_d64": 1024, "docs128k_zigzag_cp4_h32_d128": 512,
+                "zigzag1m_cp8_h32kv8_d128": 128}
 
 
-@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128", "contig128k_h16kv2_d64", "docs128k_zigzag_cp4_h32_d128", "zigzag1m_cp8_h32kv8_d128"])
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
 def test_full_size_sampled(torch_cuda, orc, name):
     from context_long_sequence_amd.share import share_from_workload
     from synth import WORKLOADS

@@ -24,7 +24,8 @@ def test_matches_oracle(orc, layout, S, cpn):
 
 
 def test_documents_match_oracle(orc):
-    for wl in (WORKLOADS["docs128k_zigzag_cp4_h32_d128"], WORKLOADS["docs128k_zigzag_cp4_h32_d128"].scaled(seed=77), WORKLOADS["docs128k_zigzag_cp4_h32_d128"].scaled(seed=4242)):
+    docs = WORKLOADS["docs128k_zigzag_cp4_h32_d128"]
+    for wl in (docs, docs.scaled(seed=77), docs.scaled(seed=4242)):
         docs = wl.doc_lens()
         assert docs.sum() == wl.S and np.all(docs % (2 * wl.cp) == 0)
         cu = np.concatenate([[0], np.cumsum(docs)]).astype(np.int32)

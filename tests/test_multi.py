@@ -22,7 +22,8 @@ def orc():
     return oracle.get()
 
 
-@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64", "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128"])
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64",
+                                  "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128"])
 def test_fused_all_rows(torch_cuda, orc, name):
     from context_long_sequence_amd.share import share_from_workload
     from test_gpu_parity import O_TOL_BF16, O_TOL_F32, _reduced, compare, oracle_share, say, to_np
