@@ -117,6 +117,13 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _pos_len(t, n, name):
+    """A position array must be 1-D with one entry per token: the kernels read
+    n of them and cannot see the array's length."""
+    if t is not None and (t.dim() != 1 or t.numel() != n):
+        raise CpattnError(2, "%s must be 1-D with %d entries, got shape %s" % (name, n, tuple(t.shape)))
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -161,6 +168,8 @@ def cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0
     lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
     if tuple(v.shape) != tuple(k.shape):
         raise CpattnError(2, "v must have k's shape")
+    _pos_len(q_pos, lq, "q_pos")
+    _pos_len(k_pos, lk, "k_pos")
     st = lib.cpattn_partial(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq, lk, hq,
                             hkv, d, _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
                             int(bool(causal)), float(softmax_scale), _dev(o, "o"), _dtype_code(o),
@@ -176,6 +185,10 @@ def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_sca
     lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
     if tuple(v.shape) != tuple(k.shape):
         raise CpattnError(2, "v must have k's shape")
+    _pos_len(q_pos, lq, "q_pos")
+    _pos_len(k_pos, lk, "k_pos")
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise CpattnError(2, "cu_seqlens must be 1-D with n_seqs + 1 >= 2 entries")
     st = lib.cpattn_varlen_partial(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq,
                                    lk, hq, hkv, d, _dev(q_pos, "q_pos", torch.int32),
                                    _dev(k_pos, "k_pos", torch.int32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
@@ -193,10 +206,12 @@ def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, cau
     n = len(k_blocks)
     if n == 0 or len(v_blocks) != n or len(k_pos_blocks) != n:
         raise CpattnError(5, "k_blocks, v_blocks and k_pos_blocks must be non-empty lists of one length")
-    for k, v in zip(k_blocks, v_blocks):
+    for k, v, p in zip(k_blocks, v_blocks, k_pos_blocks):
         _shapes(q, k, o, lse)
         if tuple(v.shape) != tuple(k.shape):
             raise CpattnError(2, "each v must have its k's shape")
+        _pos_len(p, k.shape[0], "k_pos")
+    _pos_len(q_pos, q.shape[0], "q_pos")
     ptrs = ctypes.c_void_p * n
     kp = ptrs(*[_dev(k, "k", q.dtype) for k in k_blocks])
     vp_ = ptrs(*[_dev(v, "v", q.dtype) for v in v_blocks])
@@ -264,6 +279,8 @@ def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, caus
         raise CpattnError(2, "dq must be [lq, hq, d] and dk, dv [lk, hkv, d]")
     if dout.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
         raise CpattnError(3, "q, k, v and dout must share one dtype")
+    _pos_len(q_pos, lq, "q_pos")
+    _pos_len(k_pos, lk, "k_pos")
     st = lib.cpattn_partial_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dtype_code(q), lq, lk,
                                 hq, hkv, d, _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
                                 int(bool(causal)), _dev(cu_seqlens, "cu_seqlens", torch.int32),

@@ -170,3 +170,27 @@ def test_last_error_is_thread_local(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(cp.CpattnError):
         cp.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_rejects_position_arrays_of_the_wrong_length():
+    """The kernels read lq (lk) positions and cannot see an array's length, so
+    the binding checks it before anything reaches the library."""
+    import torch
+    q = torch.zeros((8, 2, 64), dtype=torch.bfloat16)
+    k = torch.zeros((5, 2, 64), dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((2, 8), dtype=torch.float32)
+    good_q, good_k = torch.arange(8, dtype=torch.int32), torch.arange(5, dtype=torch.int32)
+    short = torch.arange(4, dtype=torch.int32)
+    for qp, kp in ((short, good_k), (good_q, short), (good_q.reshape(2, 4), good_k)):
+        with pytest.raises(cp.CpattnError) as e:
+            cp.cpattn_partial(q, k, k, qp, kp, o, lse)
+        assert e.value.status == 2 and "entries" in str(e.value)
+    with pytest.raises(cp.CpattnError):
+        cp.cpattn_varlen_partial(q, k, k, good_q, short, torch.tensor([0, 8], dtype=torch.int32), o, lse)
+    with pytest.raises(cp.CpattnError):
+        cp.cpattn_partial_multi(q, [k], [k], good_q, [short], o, lse)
+    g = torch.zeros((8, 2, 64), dtype=torch.float32)
+    gk = torch.zeros((5, 2, 64), dtype=torch.float32)
+    with pytest.raises(cp.CpattnError):
+        cp.cpattn_partial_bwd(q, k, k, q, short, good_k, lse, lse, g, gk, gk)
