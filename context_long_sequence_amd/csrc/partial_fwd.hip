@@ -42,9 +42,18 @@
 //    ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
 //    column — the V^T operand layout.
 //  * Softmax runs in base 2 with the scale folded into one FMA per score.
-//    The running max is raised only when a tile's max exceeds it by more than
-//    2^8, so the O rescale is skipped on most tiles (the final normalisation
-//    uses the same stale max, so the result is unchanged).
+//    The scores are exponentiated against the running max as it stands; no
+//    row max is formed unless a lane's sum of the tile's probabilities
+//    exceeds a bound (a new maximum) or a row has seen no key yet. Then the
+//    tile's max is formed, the running max raised if the tile's exceeds it by
+//    more than 2^8, and the exponentials taken again, so the O rescale is
+//    rare (the final normalisation uses the same stale max, so the result is
+//    unchanged).
+//  * The operands of a matrix phase (V^T for P V, then K for the next
+//    scores) are read from LDS as one stream a few MFMAs ahead, and the first
+//    few are read at the end of the vector phase before it, so the matrix
+//    cores do not wait for LDS at the start of a phase or between its two
+//    products.
 //  * The workgroup loads only the key range its rows can see; each wave masks
 //    only tiles it does not see in full (tiles it cannot see at all are
 //    computed and fully masked: within a workgroup's range that is at most a
@@ -370,6 +379,72 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     }
   };
 
+  // ---- bf16 matrix step: one operand stream over P V (tile t) then Q K^T (tile t+1) ----
+  // The MFMAs of a matrix step read one operand each from LDS (V^T for P V,
+  // K for Q K^T). They are read as a single stream, RING operands ahead of
+  // the MFMA that uses them, so the first K operands are already in flight
+  // while the last P V MFMAs run, and the first RING operands of a step are
+  // read at the end of the vector step before it (its V tile was published
+  // two barriers earlier), so the matrix cores do not wait for LDS at the
+  // start of a step either.
+  constexpr int RING = 6;
+  constexpr int NPV = 2 * NB * NDT;       // MFMAs of P V per tile
+  constexpr int NQK = NQ * NB;            // MFMAs of Q K^T per tile
+  static_assert(!C::kBf16 || RING <= NPV, "the prefetched operands are V^T operands");
+  bf16x8_t ring[RING];
+  // operand u of a step: u < NPV: V^T block (jb, hf, dt) = keys 32jb + 16hf + vr (and + 8),
+  // column block dt; otherwise K block s = u - NPV (row li of 32-key block s % NB, chunk 2(s / NB) + g)
+  auto rd_op = [&](int u, const char CPATTN_LDS* vl, const char CPATTN_LDS* kl) __attribute__((always_inline)) {
+    if constexpr (!C::kBf16) return bf16x8_t{};
+    if (u < NPV) {
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const int jb = u / (2 * NDT), hf = (u / NDT) % 2, dt = u % NDT;
+      const int roff = (32 * jb + 16 * hf) * C::kRowBytes;
+      i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t CPATTN_LDS*)(vl + vaddr[dt] + roff));
+      i16x4_t t1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t CPATTN_LDS*)(vl + vaddr[dt] + roff + 8 * C::kRowBytes));
+      return __builtin_bit_cast(bf16x8_t, (i16x8)__builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const int s = u - NPV;
+    return *(const bf16x8_t CPATTN_LDS*)(kl + kaddr[s / NB] + (s % NB) * 32 * C::kRowBytes);
+  };
+  // the first RING operands of the next step (its V^T operands), issued before the phase barrier
+  auto prefetch_step = [&](const char CPATTN_LDS* vl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) ring[u] = rd_op(u, vl, nullptr);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // MFMAs u0 .. u1-1 of a step (u0 = 0: P V first; u1 = NPV: no Q K^T; u0 = NPV: Q K^T only).
+  // With `primed` the ring already holds operands u0 .. u0+RING-1.
+  auto run_step = [&](const char CPATTN_LDS* vl, const char CPATTN_LDS* kl, auto u0c, auto u1c, bool primed)
+      __attribute__((always_inline)) {
+    constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    if (!primed) {
+#pragma unroll
+      for (int u = u0; u < u0 + RING && u < u1; ++u) ring[(u - u0) % RING] = rd_op(u, vl, kl);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = u0; u < u1; ++u) {
+      const int slot = (u - u0) % RING;
+      if (u < NPV) {
+        const int jb = u / (2 * NDT), hf = (u / NDT) % 2, dt = u % NDT;
+        const u32x4 bw = {pk[jb][4 * hf], pk[jb][4 * hf + 1], pk[jb][4 * hf + 2], pk[jb][4 * hf + 3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[slot], __builtin_bit_cast(bf16x8_t, bw), oacc[dt], 0,
+                                                           0, 0);
+      } else if constexpr (C::kBf16) {
+        // (the first k-step of each key block starts from zero, so the scores'
+        // registers are not live while P V still holds P)
+        const int s = u - NPV;
+        sacc[s % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[slot], qreg[s / NB],
+                                                               s < NB ? f32x16_t{} : sacc[s % NB], 0, 0, 0);
+      }
+      if (u + RING < u1) ring[slot] = rd_op(u + RING, vl, kl);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // ---- vector phase: mask, max, rescale, exp, sum, pack of tile t's scores ----
   // Boundary tiles: lane register r of block jb is key 32jb + 8(r/4) + 4g + r%4
   // of the tile. Keys at or past lk and keys the lane's row cannot see get -inf.
@@ -395,8 +470,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         }
       }
   };
-  auto softmax_tile = [&](const int32_t CPATTN_LDS* kp, int t) __attribute__((always_inline)) {
-    if (!tile_full(t)) mask(kp, t);
+  // Raise the running max where tile t's max exceeds it by more than kTau
+  // (base 2), rescaling the running sum and O accordingly.
+  auto raise_max = [&]() __attribute__((always_inline)) {
     float mx = neg_inf();
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
@@ -414,14 +490,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+  };
+  // exp2(scale*log2(e)*score - m) of the lane's scores: packed to bf16 as the
+  // P operand (float32 inputs: written over the scores); returns their sum
+  auto exps = [&](float m) __attribute__((always_inline)) -> float {
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], p.scale_log2, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r + 1], p.scale_log2, -m_use));
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], p.scale_log2, -m));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r + 1], p.scale_log2, -m));
         ls0 += e0;
         ls1 += e1;
         if constexpr (C::kBf16) {
@@ -431,7 +510,35 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
           sacc[jb][r + 1] = e1;
         }
       }
-    l_run += ls0 + ls1;
+    return ls0 + ls1;
+  };
+  // A lane's partial row sum of a tile (16*NB probabilities) bounds each of
+  // them, so a sum of at most 16*NB*2^kTau keeps every probability within
+  // 2^(kTau + log2(16*NB)): the running max may then lag the true one by that
+  // much, which only scales the accumulator and the sum alike.
+  constexpr float kSumLim = 16.0f * NB * (float)(1 << (int)kTau);
+  auto softmax_tile = [&](const int32_t CPATTN_LDS* kp, int t) __attribute__((always_inline)) {
+    if (!tile_full(t)) mask(kp, t);
+    float ls = 0.f;
+    if constexpr (C::kBf16) {
+      // Common case: exponentiate against the running max as it stands (no
+      // row max is formed). If a lane's sum exceeds the bound (a new maximum,
+      // or an overflow), or a row has seen no key yet, the wave forms the
+      // tile's max, raises the running max and takes the exponentials again
+      // (the scores are still in sacc); after a raise the sum is within the
+      // bound, so there are at most two passes.
+      bool redo = __builtin_amdgcn_ballot_w64(m_run == neg_inf()) != 0;
+      for (int pass = 0; pass < 2; ++pass) {
+        if (redo) raise_max();
+        ls = exps((m_run == neg_inf()) ? 0.f : m_run);
+        redo = __builtin_amdgcn_ballot_w64(!(ls <= kSumLim)) != 0;
+        if (!redo) break;
+      }
+    } else {
+      raise_max();
+      ls = exps((m_run == neg_inf()) ? 0.f : m_run);
+    }
+    l_run += ls;
     // the vector phase's results exist before the barrier that follows it
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
@@ -458,8 +565,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // follows publishes the commit; its first readers (the matrix step of t+2,
   // the vector step of t+3) are at least one more barrier away for both
   // groups.
-  auto iteration = [&](int t, auto sk) __attribute__((always_inline)) {
+  using U0 = std::integral_constant<int, 0>;
+  using UPV = std::integral_constant<int, NPV>;
+  using UPQ = std::integral_constant<int, NPV + NQK>;
+  // (`last`: tile t is the workgroup's last, so the step has no scores to form)
+  auto iteration = [&](int t, auto sk, auto last) __attribute__((always_inline)) {
     constexpr int k = decltype(sk)::value;
+    constexpr bool LAST = decltype(last)::value;
     const std::integral_constant<int, (k + 1) % NS> sn{};
     const std::integral_constant<int, (k + 2) % NS> s2{};
     const std::integral_constant<int, (k + 3) % NS> s3{};
@@ -468,10 +580,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       // (t = k mod 4, so the parities are compile-time constants)
       fetch_group(t + 3, std::integral_constant<int, (k + 3) & 1>{});
       softmax_tile(pst(sk), t);
-      phase_barrier();
+      prefetch_step(vst(sk));
+      phase_barrier_reads();
       __builtin_amdgcn_s_setprio(1);
-      pv_tile(vst(sk));
-      if (t + 1 < nt) qk_tile(kst(sn));
+      if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true);
+      else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true);
       commit_group(s3, s2, std::integral_constant<int, (k + 2) & 1>{});  // (zeros past the tiles, into free stages)
       __builtin_amdgcn_s_setprio(0);
       phase_barrier();
@@ -479,10 +592,18 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       const std::integral_constant<int, 0> set0{};
       if (t + 2 < nt) fetch_group(t + 2, set0);
       softmax_tile(pst(sk), t);
-      phase_barrier();
-      __builtin_amdgcn_s_setprio(1);
-      pv_tile(vst(sk));
-      if (t + 1 < nt) qk_tile(kst(sn));
+      if constexpr (C::kBf16) {
+        prefetch_step(vst(sk));
+        phase_barrier_reads();
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true);
+        else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true);
+      } else {
+        phase_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        pv_tile(vst(sk));
+        if constexpr (!LAST) qk_tile(kst(sn));
+      }
       if (t + 2 < nt) commit_group(s3, s2, set0);
       // Nothing is in flight here (the commit waited for its loads). Saying so
       // unconditionally keeps the compiler's wait analysis exact across the
@@ -553,13 +674,28 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
     if constexpr (kDeep) fetch_group(2, std::integral_constant<int, 0>{});  // G(2), committed in iteration 0
-    qk_tile(kst(S0{}));
+    if constexpr (C::kBf16) run_step(vst(S0{}), kst(S0{}), UPV{}, UPQ{}, false);
+    else qk_tile(kst(S0{}));
     if (grp1) phase_barrier();
-    for (int t = 0; t < nt; t += NS) {
-      iteration(t, S0{});
-      if (t + 1 < nt) iteration(t + 1, S1{});
-      if (t + 2 < nt) iteration(t + 2, S2{});
-      if (t + 3 < nt) iteration(t + 3, S3{});
+    // tiles followed by another, then the last one (peeled, so that the
+    // loop's matrix steps all have the same shape; a multi-block call runs
+    // every tile through the loop instead, forming scores of a stale stage
+    // after its last tile, which its registers cannot otherwise afford)
+    using More = std::false_type;
+    using Last = std::true_type;
+    const int nmore = MULTI ? nt : nt - 1;
+    for (int t = 0; t < nmore; t += NS) {
+      iteration(t, S0{}, More{});
+      if (t + 1 < nmore) iteration(t + 1, S1{}, More{});
+      if (t + 2 < nmore) iteration(t + 2, S2{}, More{});
+      if (t + 3 < nmore) iteration(t + 3, S3{}, More{});
+    }
+    if constexpr (!MULTI)
+    switch (nmore & 3) {
+      case 0: iteration(nmore, S0{}, Last{}); break;
+      case 1: iteration(nmore, S1{}, Last{}); break;
+      case 2: iteration(nmore, S2{}, Last{}); break;
+      default: iteration(nmore, S3{}, Last{}); break;
     }
     // (after this barrier no wave reads the ring, so the next block may refill it)
     if (!grp1) phase_barrier();

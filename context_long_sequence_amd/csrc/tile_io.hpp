@@ -205,6 +205,11 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // moving memory accesses across.
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Workgroup barrier at the end of a phase that issued only LDS reads whose
+// stages no wave rewrites before this wave's next phase_barrier() (which waits
+// for them): the reads stay in flight across it.
+__device__ __forceinline__ void phase_barrier_reads() { asm volatile("s_barrier" ::: "memory"); }
+
 // Materialise a register value at this point of the program. The barrier above
 // only orders memory accesses: left alone, the compiler sinks pure register
 // work (the exponentials, packs and row sums of the vector phase) past it into
