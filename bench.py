@@ -190,10 +190,16 @@ def main():
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     kernel_flops = step_flops * args.steps / n_launch
-    kernel_ms = float(launch_ms.mean())
+    # the kernel's mean duration for the roofline: the timed region's time per
+    # launch (launches run back to back on one stream, so this includes the
+    # short gaps between them and bounds the mean duration from above); the
+    # per-launch event pairs of the second pass are reported beside it (each
+    # pair adds its own overhead, so they are not used)
+    kernel_ms = ms_per_step / len(order)
     achieved = kernel_flops / (kernel_ms * 1e-3) / 1e12
-    log("%.3f ms/step (wall %.3f ms/step), %.1f TFLOP/s, kernel mean %.3f ms/launch (%.3f ms/step with an "
-        "event pair around every launch)" % (ms_per_step, t_wall * 1e3 / args.steps, tflops, kernel_ms, evented_ms))
+    log("%.3f ms/step (wall %.3f ms/step), %.1f TFLOP/s, %.4f ms per launch (event pairs around every launch: "
+        "mean %.4f ms, %.3f ms/step)" % (ms_per_step, t_wall * 1e3 / args.steps, tflops, kernel_ms,
+                                        float(launch_ms.mean()), evented_ms))
 
     out = {
         "metric": METRIC,
@@ -229,7 +235,9 @@ def main():
             "traffic": profiled_traffic(wl.name),
             "flop_per_launch": kernel_flops,
             "mean_launch_ms": round(kernel_ms, 5),
+            "mean_launch_ms_from": "timed region / launches (includes the gaps between launches)",
             "launches": n_launch,
+            "mean_launch_ms_event_pairs": round(float(launch_ms.mean()), 5),
             "ms_per_step_with_launch_events": round(evented_ms, 4),
         },
     }
@@ -407,23 +415,35 @@ def calibrate_copy(mib, reps=5):
           flush=True)
 
 
+def oracle_block_positions(orc, wl, docs):
+    """Each KV block's positions from the oracle's own closed forms (rank b's
+    share; the b-th contiguous chunk, i.e. the contiguous split with
+    cp = n_blocks; or the whole sequence, the contiguous split with cp = 1)."""
+    if wl.block_kind == "rank_shares":
+        return [orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0] for b in range(wl.n_blocks)]
+    if wl.block_kind == "chunks":
+        return [orc.local_positions(wl.S, wl.n_blocks, b, "contiguous")[0] for b in range(wl.n_blocks)]
+    return [orc.local_positions(wl.S, 1, 0, "contiguous")[0]]
+
+
+def oracle_threads():
+    """(threads the oracle runs on, cores in this process's affinity mask).
+    The threads are the cores of the affinity mask, capped at OMP_NUM_THREADS
+    when that is set (a GPU host's CPU share per GPU), else at 16."""
+    cores = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return max(1, min(cores, cap)), cores
+
+
 def cpu_baseline(wl, share, seconds):
     """Time the fp64 oracle on a bounded sample of the same workload's rows,
     and check the GPU output on that sample."""
     import oracle
     orc = oracle.get()
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads, affinity_cores = oracle_threads()
     docs = wl.doc_lens()
     qp, qst = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
-    kps = []
-    for b in range(wl.n_blocks):
-        if wl.block_kind == "rank_shares":
-            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
-        elif wl.block_kind == "chunks":
-            c = wl.S // wl.n_blocks
-            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
-        else:
-            kps.append(np.arange(wl.S, dtype=np.int32))
+    kps = oracle_block_positions(orc, wl, docs)
     log("cpu baseline: loading inputs on the host")
     q = wl.q()
     k = np.concatenate([wl.kv_block(b, "k") for b in range(wl.n_blocks)])
@@ -451,6 +471,7 @@ def cpu_baseline(wl, share, seconds):
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cores_in_affinity_mask": affinity_cores,
         "kind": "oracle",
         "sample": "%d sampled (query row, head) pairs of this workload against all its keys, fp64 two-pass "
                   "softmax attention, %.1f s" % (len(rows), dt),
@@ -467,18 +488,10 @@ def cpu_baseline_bwd(wl, share, dout_host, seconds):
     import oracle
     from synth import bf16_bits_to_f32
     orc = oracle.get()
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads, affinity_cores = oracle_threads()
     docs = wl.doc_lens()
     qp, qst = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
-    kps = []
-    for b in range(wl.n_blocks):
-        if wl.block_kind == "rank_shares":
-            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
-        elif wl.block_kind == "chunks":
-            c = wl.S // wl.n_blocks
-            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
-        else:
-            kps.append(np.arange(wl.S, dtype=np.int32))
+    kps = oracle_block_positions(orc, wl, docs)
     log("cpu baseline (backward): loading inputs on the host")
     q = wl.q()
     k = np.concatenate([wl.kv_block(b, "k") for b in range(wl.n_blocks)])
@@ -509,6 +522,7 @@ def cpu_baseline_bwd(wl, share, dout_host, seconds):
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cores_in_affinity_mask": affinity_cores,
         "kind": "oracle",
         "sample": "dQ of %d sampled (query row, head) pairs of this workload against all its keys, fp64, "
                   "8 d flop per visible pair (scores, O, dP, dQ), %.1f s" % (len(rows), dt),

@@ -210,6 +210,11 @@ def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, cau
         _shapes(q, k, o, lse)
         if tuple(v.shape) != tuple(k.shape):
             raise CpattnError(2, "each v must have its k's shape")
+        # the C ABI takes one KV head count for every block (it sizes each
+        # block's rows with it), so blocks that differ are rejected here
+        if k.shape[1] != k_blocks[0].shape[1]:
+            raise CpattnError(2, "every KV block must have the same number of KV heads (%d and %d)" % (
+                k_blocks[0].shape[1], k.shape[1]))
         _pos_len(p, k.shape[0], "k_pos")
     _pos_len(q_pos, q.shape[0], "q_pos")
     ptrs = ctypes.c_void_p * n

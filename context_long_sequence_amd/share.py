@@ -21,14 +21,17 @@ def bits_to_device(a, device="cuda"):
 
 
 def block_positions(S, cp, n_blocks, block_kind, layout, cu_seqlens=None):
-    """Global positions of every KV block's tokens, in block-id order (int32 numpy arrays)."""
+    """Global positions of every KV block's tokens, in block-id order (int32
+    numpy arrays), all from the library's index builder: rank b's share under
+    the workload's layout ('rank_shares'), the b-th of n_blocks equal
+    contiguous chunks ('chunks': the contiguous split with cp = n_blocks), or
+    the whole sequence ('whole': the contiguous split with cp = 1)."""
     if block_kind == "rank_shares":
         return [cpattn_zigzag_index(S, cp, b, layout, cu_seqlens)[0] for b in range(n_blocks)]
     if block_kind == "chunks":
-        c = S // n_blocks
-        return [np.arange(b * c, (b + 1) * c, dtype=np.int32) for b in range(n_blocks)]
+        return [cpattn_zigzag_index(S, n_blocks, b, "contiguous")[0] for b in range(n_blocks)]
     if block_kind == "whole":
-        return [np.arange(S, dtype=np.int32)]
+        return [cpattn_zigzag_index(S, 1, 0, "contiguous")[0]]
     raise ValueError(block_kind)
 
 

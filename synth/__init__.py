@@ -144,9 +144,10 @@ class Workload:
         return np.concatenate(parts, axis=0)
 
     def sample_pairs(self, n_pairs=None, chunk=None):
-        """(rows, heads) to check: stratified evenly over heads, uniform over
-        local tokens, always including the first and last token of each chunk
-        of `chunk` local tokens (default: the rank's two zig-zag halves)."""
+        """(rows, heads) to check, stratified evenly over heads: for every head
+        the first and last token of each chunk of `chunk` local tokens (default:
+        the rank's two zig-zag halves), plus n_pairs // hq interior tokens drawn
+        uniformly from the rest. n_pairs = 0 (and no sampled_rows): every pair."""
         n_pairs = n_pairs or self.sampled_rows
         if not n_pairs:
             r = np.repeat(np.arange(self.lq, dtype=np.int64), self.hq)
@@ -154,12 +155,14 @@ class Workload:
             return r, h
         rng = np.random.default_rng(self.seed + 2000)
         chunk = chunk or max(1, self.lq // 2)
-        ends = sorted({e for c0 in range(0, self.lq, chunk) for e in (c0, min(c0 + chunk, self.lq) - 1)})
-        per_head = max(len(ends), n_pairs // self.hq)
+        ends = np.array(sorted({e for c0 in range(0, self.lq, chunk) for e in (c0, min(c0 + chunk, self.lq) - 1)}),
+                        np.int64)
+        interior = np.setdiff1d(np.arange(self.lq, dtype=np.int64), ends)
+        per_head = min(max(1, n_pairs // self.hq), len(interior))
         rows, heads = [], []
         for h in range(self.hq):
-            extra = rng.choice(self.lq, size=per_head - len(ends), replace=False)
-            rr = np.unique(np.concatenate([np.array(ends, np.int64), extra.astype(np.int64)]))
+            extra = rng.choice(interior, size=per_head, replace=False)
+            rr = np.unique(np.concatenate([ends, extra.astype(np.int64)]))
             rows.append(rr)
             heads.append(np.full(len(rr), h, np.int32))
         return np.concatenate(rows), np.concatenate(heads)

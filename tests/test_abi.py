@@ -194,3 +194,20 @@ def test_binding_rejects_position_arrays_of_the_wrong_length():
     gk = torch.zeros((5, 2, 64), dtype=torch.float32)
     with pytest.raises(cp.CpattnError):
         cp.cpattn_partial_bwd(q, k, k, q, short, good_k, lse, lse, g, gk, gk)
+
+
+def test_binding_rejects_multi_blocks_with_different_kv_heads():
+    """cpattn_partial_multi takes one KV head count for all blocks and sizes
+    every block's rows with it; a block with fewer KV heads than the first
+    would be read past its end, so the binding rejects the call first."""
+    import torch
+    q = torch.zeros((8, 2, 64), dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((2, 8), dtype=torch.float32)
+    k2 = torch.zeros((5, 2, 64), dtype=torch.bfloat16)
+    k1 = torch.zeros((5, 1, 64), dtype=torch.bfloat16)
+    qp, kp = torch.arange(8, dtype=torch.int32), torch.arange(5, dtype=torch.int32)
+    for blocks in ([k2, k1], [k1, k2]):
+        with pytest.raises(cp.CpattnError) as e:
+            cp.cpattn_partial_multi(q, blocks, blocks, qp, [kp, kp], o, lse)
+        assert e.value.status == 2 and "KV heads" in str(e.value)

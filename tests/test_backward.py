@@ -13,7 +13,7 @@ reference that is exactly zero by cancellation must come out below 1e-5.
 import numpy as np
 import pytest
 
-from test_gpu_parity import say
+from test_gpu_parity import oracle_block_positions, record, say
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,8 @@ def grad_compare(got, ref, what):
     rms_err = float(np.sqrt(np.mean((got - ref) ** 2))) if ref.size else 0.0
     say("%s: max err %.3e of max %.3e (%.2e), rms err %.3e of rms %.3e (%.2e)" % (
         what, err, scale, err / scale if scale else 0.0, rms_err, rms_ref, rms_err / rms_ref if rms_ref else 0.0))
+    record(what, elements=int(ref.size), max_abs_err=err, max_abs_ref=scale, rms_err=rms_err, rms_ref=rms_ref,
+           max_tol_rel=GRAD_TOL_MAX, rms_tol_rel=GRAD_TOL_RMS)
     if scale == 0.0:
         # a reference that is zero by cancellation (one visible key: dP = D, so
         # dS = 0) comes out at float32 rounding level: D and dP are summed in
@@ -62,15 +64,7 @@ def oracle_grads(orc, wl, rows=None, heads=None):
     keys of every block in block-id order); dk, dv split per block."""
     docs = wl.doc_lens()
     qp, qs = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
-    kps = []
-    for b in range(wl.n_blocks):
-        if wl.block_kind == "rank_shares":
-            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
-        elif wl.block_kind == "chunks":
-            c = wl.S // wl.n_blocks
-            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
-        else:
-            kps.append(np.arange(wl.S, dtype=np.int32))
+    kps = oracle_block_positions(orc, wl, None, docs)
     k = wl.kv_all("k")
     v = wl.kv_all("v")
     from synth import bf16_bits_to_f32
@@ -157,7 +151,9 @@ def test_backward_full_size_sampled(torch_cuda, orc, name):
     say("backward %s full size: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d,
                                                                           wl.n_blocks))
     share, dout, dq, dk, dv = _run(torch_cuda, wl)
-    rows, heads = wl.sample_pairs(n_pairs=128 if name == "zigzag1m_cp8_h32kv8_d128" else 256)
+    # dQ rows: as many as the forward checks (interior rows on top of every chunk's ends)
+    from test_gpu_parity import FULL_SAMPLES
+    rows, heads = wl.sample_pairs(n_pairs=FULL_SAMPLES.get(name, 8192))
     rdq, _, _ = oracle_grads(orc, wl, rows=rows, heads=heads)
     grad_compare(dq.cpu().numpy()[rows, heads], rdq, "%s dq (sampled)" % name)
     torch = torch_cuda

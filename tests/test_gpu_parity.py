@@ -38,25 +38,43 @@ def orc():
     return oracle.get()
 
 
+def oracle_block_positions(orc, wl, blocks=None, docs=None):
+    """Each KV block's global positions from the oracle's own closed forms:
+    rank b's share ('rank_shares'), the b-th contiguous chunk ('chunks': the
+    contiguous split with cp = n_blocks), the whole sequence ('whole')."""
+    blocks = list(range(wl.n_blocks)) if blocks is None else list(blocks)
+    out = []
+    for b in blocks:
+        if wl.block_kind == "rank_shares":
+            out.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
+        elif wl.block_kind == "chunks":
+            out.append(orc.local_positions(wl.S, wl.n_blocks, b, "contiguous")[0])
+        else:
+            out.append(orc.local_positions(wl.S, 1, 0, "contiguous")[0])
+    return out
+
+
 def oracle_share(orc, wl, rows=None, heads=None, blocks=None):
     """The oracle's result for a workload: positions from its own closed forms,
     keys of the given blocks (default all) concatenated in block-id order."""
     docs = wl.doc_lens()
     qp, qs = orc.local_positions(wl.S, wl.cp, wl.rank, wl.layout, doc_lens=docs)
     blocks = list(range(wl.n_blocks)) if blocks is None else list(blocks)
-    kps = []
-    for b in blocks:
-        if wl.block_kind == "rank_shares":
-            kps.append(orc.local_positions(wl.S, wl.cp, b, wl.layout, doc_lens=docs)[0])
-        elif wl.block_kind == "chunks":
-            c = wl.S // wl.n_blocks
-            kps.append(np.arange(b * c, (b + 1) * c, dtype=np.int32))
-        else:
-            kps.append(np.arange(wl.S, dtype=np.int32))
+    kps = oracle_block_positions(orc, wl, blocks, docs)
     k = np.concatenate([wl.kv_block(b, "k") for b in blocks])
     v = np.concatenate([wl.kv_block(b, "v") for b in blocks])
     return orc.attention(wl.q(), k, v, qp, np.concatenate(kps), qs if docs is not None else None, True,
                          rows=rows, heads=heads)
+
+
+def record(what, **fields):
+    """Append one achieved-error record (JSON) to $CPATTN_PARITY_LOG, if set."""
+    import json
+    import os
+    path = os.environ.get("CPATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(test=what, **fields)) + "\n")
 
 
 def to_np(o, lse):
@@ -79,6 +97,7 @@ def compare(o, lse, o_ref, lse_ref, rows, heads, o_tol, what, lse_tol=LSE_TOL):
     eo = float(np.max(np.abs(og - o_ref))) if og.size else 0.0
     el = float(np.max(np.abs(lg[~empty] - lse_ref[~empty]))) if (~empty).any() else 0.0
     say("%s: max|dO| = %.3e  max|dLSE| = %.3e  (%d rows)" % (what, eo, el, len(lse_ref)))
+    record(what, rows=int(len(lse_ref)), max_abs_err_o=eo, max_abs_err_lse=el, o_tol=o_tol, lse_tol=lse_tol)
     assert eo <= o_tol, "%s: O error %.3e > %.1e" % (what, eo, o_tol)
     assert el <= lse_tol, "%s: LSE error %.3e > %.1e" % (what, el, lse_tol)
     assert np.all(og[empty] == 0.0), what + ": empty rows must have O = 0"
@@ -184,8 +203,15 @@ def test_accumulate_leaves_unseeing_rows_bit_identical(torch_cuda):
     assert n_checked > 0
 
 
-FULL_SAMPLES = {"zigzag64k_cp8_h32_d128": 512, "contig128k_h16kv2_d64": 1024, "docs128k_zigzag_cp4_h32_d128": 512,
-                "zigzag1m_cp8_h32kv8_d128": 128}
+# (row, head) pairs the oracle checks at full size, interior rows drawn on top
+# of every chunk's first and last token for every head: the 128K-token GQA
+# share and the 1M-token share at the row counts their workloads state (4096,
+# 2048); the 64K share and the documents share, which the workloads ask to
+# check on every row, at 8192 (the oracle takes about 190 s per full share
+# on the test machine's cores, beyond a test's time limit; the Q = 0 closed
+# form below covers every row of every workload at full size)
+FULL_SAMPLES = {"zigzag64k_cp8_h32_d128": 8192, "contig128k_h16kv2_d64": 4096, "docs128k_zigzag_cp4_h32_d128": 8192,
+                "zigzag1m_cp8_h32kv8_d128": 2048}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLES))
@@ -213,14 +239,18 @@ def _visible_counts(q_pos, k_pos_all, q_start=None):
     return hi - lo, lo, hi
 
 
-@pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128", "docs128k_zigzag_cp4_h32_d128"])
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
 def test_full_size_zero_q_closed_form(torch_cuda, name):
-    """Q = 0 gives uniform weights: LSE = ln(#visible) for EVERY row, and O the
-    mean of the visible values (checked on sampled rows from host prefix sums)."""
+    """Q = 0 gives uniform weights: LSE = ln(#visible) for EVERY row and head,
+    and O the mean of the visible values (checked on sampled rows of a few
+    heads from host prefix sums), at full size in the benchmark's launch
+    configuration. The visible counts come from the positions on the host
+    (np.searchsorted), P = 1 and l = #visible are exact in float32 below 2^24."""
     import torch
     from context_long_sequence_amd.share import share_from_workload
     from synth import WORKLOADS, bf16_bits_to_f32
     wl = WORKLOADS[name]
+    say("%s Q=0 full size: generating inputs" % name)
     share = share_from_workload(wl)
     share.q.zero_()
     o, lse = share.step(wl.arrival(), "accumulate")
@@ -232,19 +262,31 @@ def test_full_size_zero_q_closed_form(torch_cuda, name):
     cnt, lo, hi = _visible_counts(share.q_pos_host, kp_all, qs)
     want = np.log(cnt.astype(np.float64))
     err = float(np.max(np.abs(lse - want[None, :])))
-    say("%s Q=0: max|LSE - ln(count)| = %.3e over %d rows" % (name, err, lse.size))
+    say("%s Q=0: max|LSE - ln(count)| = %.3e over %d (row, head) pairs" % (name, err, lse.size))
+    record(name + " Q=0 LSE, every row", rows=int(lse.size), max_abs_err_lse=err, lse_tol=LSE_TOL)
     assert err <= LSE_TOL
-    # O on a few rows per head: mean of the visible V rows, in position order
+    # O on sampled rows of a few heads: mean of the visible V rows, in position order
     order = np.argsort(kp_all, kind="stable")
-    v_all = np.concatenate([wl.kv_block(b, "v") for b in range(wl.n_blocks)])
     rng = np.random.default_rng(5)
     rows = rng.choice(wl.lq, size=16, replace=False)
-    for h in range(0, wl.hq, 8):
-        vh = bf16_bits_to_f32(v_all[order, h // (wl.hq // wl.hkv)]).astype(np.float64)
+    G = wl.hq // wl.hkv
+    eo = 0.0
+    for h in sorted({0, wl.hq // 2, wl.hq - 1}):
+        g = h // G
+        vg = np.concatenate([wl.kv_block(b, "v")[:, g] for b in range(wl.n_blocks)])
+        vh = bf16_bits_to_f32(vg[order]).astype(np.float64)
+        del vg
         pref = np.concatenate([np.zeros((1, wl.d)), np.cumsum(vh, axis=0)])
+        del vh
         for i in rows:
             mean = (pref[hi[i]] - pref[lo if np.isscalar(lo) else lo[i]]) / cnt[i]
-            assert np.max(np.abs(o[i, h] - mean)) <= O_TOL_BF16
+            eo = max(eo, float(np.max(np.abs(o[i, h] - mean))))
+        del pref
+    say("%s Q=0: max|O - mean of visible V| = %.3e on %d rows x 3 heads" % (name, eo, len(rows)))
+    record(name + " Q=0 O, sampled", rows=int(3 * len(rows)), max_abs_err_o=eo, o_tol=O_TOL_BF16)
+    assert eo <= O_TOL_BF16
+    del share
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
