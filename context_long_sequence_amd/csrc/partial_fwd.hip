@@ -416,8 +416,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   };
   // MFMAs u0 .. u1-1 of a step (u0 = 0: P V first; u1 = NPV: no Q K^T; u0 = NPV: Q K^T only).
   // With `primed` the ring already holds operands u0 .. u0+RING-1.
-  auto run_step = [&](const char CPATTN_LDS* vl, const char CPATTN_LDS* kl, auto u0c, auto u1c, bool primed)
-      __attribute__((always_inline)) {
+  // `mid` runs after MFMA kMid has been issued (the ring's commit, so that its
+  // LDS writes overlap the MFMAs still to come).
+  constexpr int kMid = 22;
+  auto run_step = [&](const char CPATTN_LDS* vl, const char CPATTN_LDS* kl, auto u0c, auto u1c, bool primed,
+                      auto mid) __attribute__((always_inline)) {
     constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     if (!primed) {
@@ -441,6 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
                                                                s < NB ? f32x16_t{} : sacc[s % NB], 0, 0, 0);
       }
       if (u + RING < u1) ring[slot] = rd_op(u + RING, vl, kl);
+      if (u == kMid || (u1 <= kMid && u == u1 - 1)) mid();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -583,9 +587,12 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       prefetch_step(vst(sk));
       phase_barrier_reads();
       __builtin_amdgcn_s_setprio(1);
-      if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true);
-      else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true);
-      commit_group(s3, s2, std::integral_constant<int, (k + 2) & 1>{});  // (zeros past the tiles, into free stages)
+      // (the commit, zeros past the tiles, goes into free stages mid-step)
+      auto mid = [&]() __attribute__((always_inline)) {
+        commit_group(s3, s2, std::integral_constant<int, (k + 2) & 1>{});
+      };
+      if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true, mid);
+      else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true, mid);
       __builtin_amdgcn_s_setprio(0);
       phase_barrier();
     } else {
@@ -596,15 +603,19 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         prefetch_step(vst(sk));
         phase_barrier_reads();
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true);
-        else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true);
+        // the commit of G(t+2) (stages every wave has finished with) mid-step
+        auto mid = [&]() __attribute__((always_inline)) {
+          if (t + 2 < nt) commit_group(s3, s2, set0);
+        };
+        if constexpr (LAST) run_step(vst(sk), kst(sn), U0{}, UPV{}, true, mid);
+        else run_step(vst(sk), kst(sn), U0{}, UPQ{}, true, mid);
       } else {
         phase_barrier();
         __builtin_amdgcn_s_setprio(1);
         pv_tile(vst(sk));
         if constexpr (!LAST) qk_tile(kst(sn));
+        if (t + 2 < nt) commit_group(s3, s2, set0);
       }
-      if (t + 2 < nt) commit_group(s3, s2, set0);
       // Nothing is in flight here (the commit waited for its loads). Saying so
       // unconditionally keeps the compiler's wait analysis exact across the
       // conditional fetch/commit pair: otherwise it assumes the staging
@@ -674,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
     if constexpr (kDeep) fetch_group(2, std::integral_constant<int, 0>{});  // G(2), committed in iteration 0
-    if constexpr (C::kBf16) run_step(vst(S0{}), kst(S0{}), UPV{}, UPQ{}, false);
+    if constexpr (C::kBf16) run_step(vst(S0{}), kst(S0{}), UPV{}, UPQ{}, false, []() {});
     else qk_tile(kst(S0{}));
     if (grp1) phase_barrier();
     // tiles followed by another, then the last one (peeled, so that the
@@ -710,8 +721,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
 
   float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
   float* lse_ptr = p.lse + (int64_t)h * lq + (r0 + li);
-  if (p.accumulate && row_valid) merge_weights(*lse_ptr, lse_blk, w_old, w_blk, lse_out);
-  const float s_blk = w_blk * inv_l;
+  // (the stored LSE is requested here and the stored O rows below before the
+  // merge weights are formed, so the two reads share one round trip)
+  const float lse_old = (p.accumulate && row_valid) ? *lse_ptr : neg_inf();
   if constexpr (sizeof(TOut) == 2) {
     // bf16 O goes out through LDS, which no wave reads any more: each lane
     // holds 4-column pieces of one row, so writing them straight out would
@@ -733,14 +745,21 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     const int n_rows = wave_active ? min(32, lq - r0) : 0;
     const int prow = lane / CH, pchunk = lane % CH;            // this lane's place in a pass
     if (p.accumulate) {
+      u32x4 orow[32 / RPP];
 #pragma unroll
       for (int pass = 0; pass < 32 / RPP; ++pass) {
         const int row = pass * RPP + prow;
-        if (row < n_rows)
-          *(u32x4 CPATTN_LDS*)(stg + row * RS + pchunk * 16) = *(const u32x4*)(obase + row * ostride + pchunk * 8);
+        orow[pass] = row < n_rows ? *(const u32x4*)(obase + row * ostride + pchunk * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (row_valid) merge_weights(lse_old, lse_blk, w_old, w_blk, lse_out);
+#pragma unroll
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int row = pass * RPP + prow;
+        if (row < n_rows) *(u32x4 CPATTN_LDS*)(stg + row * RS + pchunk * 16) = orow[pass];
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+    const float s_blk = w_blk * inv_l;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -766,6 +785,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         *(u32x4*)(obase + row * ostride + pchunk * 8) = *(const u32x4 CPATTN_LDS*)(stg + row * RS + pchunk * 16);
     }
   } else {
+    if (p.accumulate && row_valid) merge_weights(lse_old, lse_blk, w_old, w_blk, lse_out);
+    const float s_blk = w_blk * inv_l;
     if (row_valid) {
       TOut* orow = (TOut*)p.o + ((int64_t)(r0 + li) * p.hq + h) * D;
 #pragma unroll
