@@ -130,7 +130,9 @@ def _large(name):
 
 # The full-size documents case faulted the GPU once, in its forward step, with
 # a forward kernel that staged V transposed; that kernel was taken out, no
-# cause was shown, and the case stays off the GPU until one is. (The full-size
+# cause was shown, and the case stays off the GPU until one is. (The CPU
+# replay in test_address_replay.py finds every address of the committed
+# kernels in range at this shape.) (The full-size
 # documents forward is still compared with the oracle by the forward parity
 # tests, and the documents backward at half length here and at reduced sizes.)
 @pytest.mark.parametrize("name", ["zigzag64k_cp8_h32_d128",
@@ -211,7 +213,8 @@ def _ragged_cases():
                 if (lq, lk, hq, hkv, causal, d) == (257, 300, 3, 3, True, 64):
                     # This case faulted the GPU once, with a query-gradient kernel that
                     # fetched two tiles ahead; that kernel was taken out, no cause was
-                    # shown, and the case stays off the GPU until one is.
+                    # shown, and the case stays off the GPU until one is (the CPU replay
+                    # in test_address_replay.py finds the committed kernels in range here).
                     marks = (pytest.mark.skip(reason="faulted the GPU with an earlier query-kernel variant; "
                                                      "cause not yet shown"),)
                 out.append(pytest.param(d, causal, lq, lk, hq, hkv, marks=marks,
