@@ -33,7 +33,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "cpattn.h")
 CPATTN_BF16, CPATTN_F32 = 0, 1
 LAYOUTS = {"contiguous": 0, "zigzag": 1, "striped": 2}
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSORTED", 5: "ERR_RANGE",
-          6: "ERR_ALIGN", 7: "ERR_ALIAS", 8: "ERR_HIP"}
+          6: "ERR_HIP", 7: "ERR_ALIGN", 8: "ERR_ALIAS"}
 
 
 class CpattnError(RuntimeError):

@@ -56,9 +56,9 @@ typedef enum {
     CPATTN_ERR_DTYPE = 3,     /* unsupported dtype or dtype combination */
     CPATTN_ERR_UNSORTED = 4,  /* positions or offsets not ascending */
     CPATTN_ERR_RANGE = 5,     /* rank, cp size, layout or flag out of range */
-    CPATTN_ERR_ALIGN = 6,     /* a pointer is misaligned (16 bytes for tensors, 4 for int32/float32 arrays) */
-    CPATTN_ERR_ALIAS = 7,     /* an output overlaps an input */
-    CPATTN_ERR_HIP = 8        /* a HIP runtime call failed; the message holds hipGetErrorString */
+    CPATTN_ERR_HIP = 6,       /* a HIP runtime call failed; the message holds hipGetErrorString */
+    CPATTN_ERR_ALIGN = 7,     /* a pointer is misaligned (16 bytes for tensors, 4 for int32/float32 arrays) */
+    CPATTN_ERR_ALIAS = 8      /* an output overlaps an input */
 } cpattn_status;
 
 typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
@@ -129,7 +129,13 @@ cpattn_status cpattn_partial(const void *q, const void *k, const void *v, cpattn
                              void *o, cpattn_dtype o_dtype, float *lse, int32_t accumulate, void *stream);
 
 /*
- * As cpattn_partial with causal == 1, for packed variable-length documents:
+ * As cpattn_partial with causal == 1, for packed variable-length documents.
+ * Ranks whose sequences differ in length (variable-length data) are named by
+ * the FCP page ("从固定环到自由拓扑：FCP到底在解决什么", §3.2, the
+ * load-balanced graph construction), and packing several documents into one
+ * training sequence is the Halo page's packing option ("长上下文训练 256k
+ * 不难", its SFT launch commands); a token then attends only within its own
+ * document, causally. Here:
  * cu_seqlens (DEVICE memory, n_seqs+1 ascending global packed offsets,
  * cu_seqlens[0] == 0) says where each document starts, and key j is visible to
  * row i iff seq_start(q_pos[i]) <= k_pos[j] <= q_pos[i], where seq_start(p) is

@@ -211,3 +211,13 @@ def test_binding_rejects_multi_blocks_with_different_kv_heads():
         with pytest.raises(cp.CpattnError) as e:
             cp.cpattn_partial_multi(q, blocks, blocks, qp, [kp, kp], o, lse)
         assert e.value.status == 2 and "KV heads" in str(e.value)
+
+
+def test_status_table_matches_the_header():
+    """The binding's status names carry the values the header's enum gives them."""
+    import re
+    with open(cp.HEADER) as f:
+        text = f.read()
+    enum = text[text.index("typedef enum {"):text.index("} cpattn_status;")]
+    pairs = {int(v): k for k, v in re.findall(r"CPATTN_(\w+)\s*=\s*(\d+)", enum)}
+    assert pairs == cp.STATUS
