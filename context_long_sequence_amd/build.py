@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcpattn.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["partial_fwd.hip", "partial_bwd.hip", "merge_lse.hip"]
+HIP_SOURCES = ["partial_fwd.hip", "partial_bwd.hip", "partial_bwd_f32.hip", "merge_lse.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]

@@ -317,14 +317,16 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
     if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
     if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
   }
-  if (in_dtype != CPATTN_BF16) return fail(CPATTN_ERR_DTYPE, "the backward takes bf16 q, k, v and dout");
+  if (in_dtype != CPATTN_BF16 && in_dtype != CPATTN_F32)
+    return fail(CPATTN_ERR_DTYPE, "q, k, v and dout must be bf16 or float32");
   if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
   if (hq < 1 || hkv < 1) return fail(CPATTN_ERR_SHAPE, "hq and hkv must be >= 1 (hq=%d hkv=%d)", hq, hkv);
   if (hq % hkv) return fail(CPATTN_ERR_SHAPE, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
   if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
   if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
   // a 32-row tile of one head is addressed with 32-bit buffer offsets
-  if ((int64_t)hq * head_dim * 2 * 32 >= (int64_t)1 << 31)
+  const int64_t esz = dsize(in_dtype);
+  if ((int64_t)hq * head_dim * esz * 32 >= (int64_t)1 << 31)
     return fail(CPATTN_ERR_SHAPE, "hq * head_dim too large (a 32-row tile must span < 2 GiB)");
   if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
@@ -332,7 +334,7 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
     return fail(CPATTN_ERR_ALIGN, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(delta, 4) || (q_pos && !aligned(q_pos, 4)) || (k_pos && !aligned(k_pos, 4)))
     return fail(CPATTN_ERR_ALIGN, "lse, delta and positions must be 4-byte aligned");
-  const size_t nq = (size_t)lq * hq * head_dim * 2, nk = (size_t)lk * hkv * head_dim * 2;
+  const size_t nq = (size_t)lq * hq * head_dim * esz, nk = (size_t)lk * hkv * head_dim * esz;
   const size_t ndq = (size_t)lq * hq * head_dim * 4, ndk = (size_t)lk * hkv * head_dim * 4;
   const size_t nl = (size_t)lq * hq * sizeof(float);
   const void* ins[] = {q, k, v, dout, lse, delta};
@@ -361,7 +363,8 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
   p.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.causal = causal; p.acc_dq = accumulate_dq; p.acc_dkv = accumulate_dkv;
-  hipError_t e = cpattn::launch_bwd(p, head_dim, cu_seqlens != nullptr, s);
+  hipError_t e = in_dtype == CPATTN_F32 ? cpattn::launch_bwd_f32(p, head_dim, cu_seqlens != nullptr, s)
+                                         : cpattn::launch_bwd(p, head_dim, cu_seqlens != nullptr, s);
   if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

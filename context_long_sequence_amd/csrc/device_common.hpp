@@ -143,6 +143,13 @@ __device__ __forceinline__ int32_t doc_start(const int32_t* cu_seqlens, int32_t 
   return cu_seqlens[idx < 0 ? 0 : idx];
 }
 
+// End of the document holding position p: the first offset > p (INT32_MAX
+// past the last one).
+__device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_seqs, int32_t p) {
+  const int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, p);
+  return idx <= n_seqs ? cu_seqlens[idx] : 0x7FFFFFFF;
+}
+
 // v_permlane32_swap exchanges the upper half-wave of its first operand with
 // the lower half-wave of its second. Passing the same value twice leaves, in
 // every lane, one result equal to the lane's own value and the other equal to

@@ -1,5 +1,6 @@
 // kernels_bwd.hpp — host-visible launch interface of the gradient kernels
-// (partial_bwd.hip) for the C-ABI layer (api.cpp). Internal to the library.
+// (partial_bwd.hip, partial_bwd_f32.hip) for the C-ABI layer (api.cpp).
+// Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,8 +29,10 @@ struct BwdParams {
   int32_t n_tiles, n_wg;      // set per kernel by launch_bwd
 };
 
-// Enqueue the key-gradient kernel (if lk > 0) then the query-gradient kernel (if lq > 0).
+// Enqueue the key-gradient kernel (if lk > 0) then the query-gradient kernel (if lq > 0):
+// bf16 q, k, v, dout (partial_bwd.hip) or float32 ones (partial_bwd_f32.hip).
 hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream);
+hipError_t launch_bwd_f32(BwdParams p, int head_dim, bool varlen, hipStream_t stream);
 
 // Enqueue delta[h][i] = <dout[i][h], o[i][h]>.
 hipError_t launch_bwd_delta(const void* o, int o_bf16, const void* dout, int do_bf16, int64_t lq, int32_t hq,

@@ -121,13 +121,6 @@ __device__ __forceinline__ void tr_offsets(int lane, int dt, int& a0, int& a8) {
   a8 = T::off(vr + 8, col >> 3) + ((col & 7) << 1);
 }
 
-// End of the document holding position x: the first offset > x (INT32_MAX
-// past the last one).
-__device__ __forceinline__ int32_t doc_end(const int32_t* cu_seqlens, int32_t n_seqs, int32_t x) {
-  const int64_t idx = upper_bound_i32(cu_seqlens, (int64_t)n_seqs + 1, x);
-  return idx <= n_seqs ? cu_seqlens[idx] : 0x7FFFFFFF;
-}
-
 // ---------------------------------------------------------------------------
 // Key kernel: dK and dV of 128 keys of one KV head.
 //

@@ -215,7 +215,7 @@ cpattn_status cpattn_bwd_delta(const void *o, cpattn_dtype o_dtype, const void *
  *                                          once every local row is seen).
  * Query heads sharing a KV head add into its dK, dV (GQA).
  *
- *  q, dout  [lq][hq][head_dim] bf16;  k, v [lk][hkv][head_dim] bf16
+ *  q, dout  [lq][hq][head_dim], k, v [lk][hkv][head_dim], all in_dtype (bf16 or float32)
  *  q_pos, k_pos, causal, cu_seqlens, n_seqs   masks as in cpattn_partial
  *                (cu_seqlens == NULL: no documents; otherwise DEVICE offsets
  *                as in cpattn_varlen_partial, and causal must be 1)
@@ -226,7 +226,8 @@ cpattn_status cpattn_bwd_delta(const void *o, cpattn_dtype o_dtype, const void *
  *  dq     [lq][hq][head_dim] float32; accumulate_dq 0: written, 1: added to
  *  dk, dv [lk][hkv][head_dim] float32; accumulate_dkv 0: written, 1: added to
  *
- * bf16 inputs only (CPATTN_ERR_DTYPE otherwise); head_dim 64 or 128;
+ * bf16 inputs run bf16 matrix products (P and dS rounded to bf16 for them),
+ * float32 inputs float32 ones (every step in float32); head_dim 64 or 128;
  * hq % hkv == 0. Outputs must not overlap the inputs or each other. lq == 0:
  * dk, dv get zeros (or are left as they are when accumulating); lk == 0
  * likewise for dq. The two kernels (keys, then queries) write disjoint

@@ -663,3 +663,126 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
         if causal and ts.size:
             idx = j0[:, None] + np.arange(32)
             mem.index("k_pos", idx[idx < lk], "dq k_pos")
+
+
+def f32_off(row, chunk):
+    """LDS byte offset of 16-byte chunk `chunk` of row `row` of a float32 gradient-kernel tile (without the row base)."""
+    return (chunk ^ (row & 15)) << 4
+
+
+def replay_backward_f32(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0):
+    """One cpattn_partial_bwd call with float32 inputs (partial_bwd_f32.hip):
+    the key kernel, then the query kernel. Tensors as in replay_backward."""
+    G = hq // hkv
+    row_bytes = 4 * D
+    kchunks = D // 4
+    tb = 32 * row_bytes
+    units = tb // 16 // 256
+    li, g = LANES & 31, LANES >> 5
+    NK, NDT = D // 2, D // 32
+    qp, kpa = sr.arrays.get("q_pos"), sr.arrays.get("k_pos")
+    tid = np.arange(256, dtype=np.int64)
+    for u in range(units):
+        unit = tid + 256 * u
+        mem.lds((unit // kchunks) * row_bytes + f32_off(unit // kchunks, unit % kchunks), 16, tb, "f32 commit")
+    for col in range(D):
+        mem.lds(np.arange(32) * row_bytes + f32_off(np.arange(32), col >> 2) + ((col & 3) << 2), 4, tb, "f32 at")
+    # ---- key kernel: workgroup = 128 keys (32 per wave) of one KV head ----
+    if lk > 0:
+        n_tiles = (lk + 127) // 128
+        n_wg = n_tiles * hkv
+        check_remap(n_wg)
+        q_stride = hq * D * 4
+        L = np.arange(n_wg, dtype=np.int64)
+        hk = L // n_tiles
+        wg_j0 = (L % n_tiles) * 128
+        wg_j1 = np.minimum(wg_j0 + 128, lk)
+        i_lo, i_hi = np.zeros(n_wg, np.int64), np.full(n_wg, lq, np.int64)
+        if causal:
+            mem.index("k_pos", wg_j0, "k_pos[wg_j0]")
+            i_lo = sr.wave_upper_bound("q_pos", lq, kpa[wg_j0].astype(np.int64) - 1)
+            if varlen:
+                mem.index("k_pos", wg_j1 - 1)
+                i_hi = sr.wave_upper_bound("q_pos", lq, sr.doc_end("cu", n_seqs, kpa[wg_j1 - 1]) - 1)
+        nqt = np.where(i_hi > i_lo, (i_hi - i_lo + 31) // 32, 0)
+        n_it = G * nqt
+        its, own = ragged_ranges(np.zeros(n_wg), n_it)  # fetch(0), then fetch(it + 1) for it + 1 < n_it
+        nq = np.maximum(nqt[own], 1)
+        hh = hk[own] * G + its // nq
+        i0 = i_lo[own] + 32 * (its % nq)
+        rows = clamp_rows(lq - i0, 32)
+        for u in range(units):
+            unit = tid + 256 * u
+            voff = (unit // kchunks) * q_stride + (unit % kchunks) * 16
+            for name in ("q", "dout"):
+                mem.buffer(name, hh * D * 4 + i0 * q_stride, rows * q_stride, voff, 16, "dkv f32 fetch")
+        r = i0[:, None] + np.arange(32)
+        ok = r < lq
+        mem.index("lse", (hh[:, None] * lq + r)[ok], "dkv f32 lse")
+        mem.index("delta", (hh[:, None] * lq + r)[ok], "dkv f32 delta")
+        if causal:
+            mem.index("q_pos", r[ok], "dkv f32 q_pos")
+        j0 = wg_j0[:, None] + 32 * np.arange(4, dtype=np.int64)[None, :]
+        kj = np.minimum(j0[..., None] + li, lk - 1)
+        key_valid = j0[..., None] + li < lk
+        hk3 = hk[:, None, None]
+        for ks in range(NK):
+            off = ((kj * hkv + hk3) * D + 2 * ks + g) * 4
+            mem.plain("k", off, 4, "dkv f32 kreg")
+            mem.plain("v", off, 4, "dkv f32 vreg")
+        if causal:
+            mem.index("k_pos", kj, "k_pos[kj]")
+            if varlen:
+                sr.doc_end("cu", n_seqs, kpa[kj])
+        for dt in range(NDT):
+            for rr in range(4):
+                off = (((kj * hkv + hk3) * D + 32 * dt + 8 * rr + 4 * g) * 4)[key_valid]
+                mem.plain("dk", off, 16, "dk")
+                mem.plain("dv", off, 16, "dv")
+    # ---- query kernel: workgroup = 128 rows (32 per wave) of one query head ----
+    if lq > 0:
+        n_tiles = (lq + 127) // 128
+        n_wg = n_tiles * hq
+        check_remap(n_wg)
+        kv_stride = hkv * D * 4
+        L = np.arange(n_wg, dtype=np.int64)
+        h = L // n_tiles
+        hk = h // G
+        wg_r0 = (n_tiles - 1 - L % n_tiles) * 128
+        wg_r1 = np.minimum(wg_r0 + 128, lq)
+        r0 = wg_r0[:, None] + 32 * np.arange(4, dtype=np.int64)[None, :]
+        qi = np.minimum(r0[..., None] + li, lq - 1)
+        row_valid = r0[..., None] + li < lq
+        h3 = h[:, None, None]
+        for ks in range(NK):
+            off = ((qi * hq + h3) * D + 2 * ks + g) * 4
+            mem.plain("q", off, 4, "dq f32 qreg")
+            mem.plain("dout", off, 4, "dq f32 dreg")
+        mem.index("lse", h3 * lq + qi, "dq lse")
+        mem.index("delta", (h3 * lq + qi)[row_valid], "dq delta")
+        if causal:
+            mem.index("q_pos", qi, "dq q_pos")
+            if varlen:
+                sr.doc_start("cu", n_seqs, qp[qi])
+        for dt in range(NDT):
+            for rr in range(4):
+                off = (((qi * hq + h3) * D + 32 * dt + 8 * rr + 4 * g) * 4)[row_valid]
+                mem.plain("dq", off, 16, "dq")
+        kb, ke = np.zeros(n_wg, np.int64), np.full(n_wg, lk, np.int64)
+        if causal:
+            mem.index("q_pos", np.stack([wg_r1 - 1, wg_r0]))
+            ke = sr.wave_upper_bound("k_pos", lk, qp[wg_r1 - 1])
+            if varlen:
+                kb = sr.wave_upper_bound("k_pos", lk, sr.doc_start("cu", n_seqs, qp[wg_r0]) - 1)
+        nt = np.where(ke > kb, (ke - kb + 31) // 32, 0)
+        ts, own = ragged_ranges(np.zeros(n_wg), nt)
+        j0 = kb[own] + 32 * ts
+        rows = clamp_rows(lk - j0, 32)
+        for u in range(units):
+            unit = tid + 256 * u
+            voff = (unit // kchunks) * kv_stride + (unit % kchunks) * 16
+            mem.buffer("k", hk[own] * D * 4 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq f32 fetch k")
+            mem.buffer("v", hk[own] * D * 4 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq f32 fetch v")
+        if causal and ts.size:
+            idx = j0[:, None] + np.arange(32)
+            mem.index("k_pos", idx[idx < lk], "dq k_pos")

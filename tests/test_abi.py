@@ -129,7 +129,7 @@ def test_backward_rejects(lib):
     assert bwd(dk=0) == STATUS["ERR_NULL"]
     assert bwd(delta=0) == STATUS["ERR_NULL"]
     assert bwd(qp=0) == STATUS["ERR_NULL"]                     # causal needs positions
-    assert bwd(dt=1) == STATUS["ERR_DTYPE"]                    # float32 inputs are not taken
+    assert bwd(dt=7) == STATUS["ERR_DTYPE"]                    # neither bf16 nor float32
     assert bwd(hd=96) == STATUS["ERR_SHAPE"]
     assert bwd(hq=6, hkv=4) == STATUS["ERR_SHAPE"]
     assert bwd(lk=1 << 31) == STATUS["ERR_SHAPE"]

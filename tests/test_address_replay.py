@@ -186,3 +186,42 @@ def test_search_model_is_an_upper_bound():
         assert np.array_equal(sr2.doc_start("cu", len(cu) - 1, x), cu[np.maximum(ub - 1, 0)])
         assert np.array_equal(sr2.doc_end("cu", len(cu) - 1, x),
                               np.where(ub < len(cu), cu[np.minimum(ub, len(cu) - 1)], ar.INT32_MAX))
+
+
+def _f32_bwd_mem(lq, lk, hq, hkv, d, cu=None):
+    return ar.Mem(q=lq * hq * d * 4, dout=lq * hq * d * 4, k=lk * hkv * d * 4, v=lk * hkv * d * 4,
+                  lse=hq * lq * 4, delta=hq * lq * 4, q_pos=lq * 4, k_pos=lk * 4, null=0,
+                  cu=0 if cu is None else len(cu) * 4, dq=lq * hq * d * 4, dk=lk * hkv * d * 4,
+                  dv=lk * hkv * d * 4)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lq,lk,hq,hkv", [(100, 77, 2, 1), (129, 200, 4, 4), (33, 1, 4, 2), (70, 130, 16, 1),
+                                          (256, 256, 1, 1), (0, 5, 2, 1), (5, 0, 2, 1)])
+def test_float32_backward_ragged(lq, lk, hq, hkv, causal, d):
+    """The float32 gradient kernels at the float32 GPU tests' shapes (and empty sides)."""
+    rng = np.random.default_rng(lq * 11 + lk + d + causal)
+    qp = np.sort(rng.choice(4 * (lq + lk) + 1, lq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(4 * (lq + lk) + 1, lk, replace=False)).astype(np.int32)
+    mem = _f32_bwd_mem(lq, lk, hq, hkv, d)
+    ar.replay_backward_f32(mem, ar.Searches(mem, {"q_pos": qp, "k_pos": kp}), lq=lq, lk=lk, hq=hq, hkv=hkv, D=d,
+                           causal=causal)
+
+
+def test_float32_backward_documents():
+    """The float32 gradient kernels on the reduced documents workloads of the float32 GPU tests."""
+    from synth import WORKLOADS
+    from context_long_sequence_amd import cpattn_zigzag_index
+    from context_long_sequence_amd.share import block_positions
+    base = WORKLOADS["docs128k_zigzag_cp4_h32_d128"]
+    for wl in [base.scaled(S=8192, hq=2, hkv=2, docs=(256, 2048), dtype="f32"),
+               base.scaled(S=4096, hq=4, hkv=1, d=64, docs=(128, 1024), dtype="f32")]:
+        cu = np.concatenate([[0], np.cumsum(wl.doc_lens())]).astype(np.int32)
+        q_pos, _ = cpattn_zigzag_index(wl.S, wl.cp, wl.rank, wl.layout, cu)
+        kps = block_positions(wl.S, wl.cp, wl.n_blocks, wl.block_kind, wl.layout, cu)
+        for kp in kps:
+            mem = _f32_bwd_mem(wl.lq, len(kp), wl.hq, wl.hkv, wl.d, cu)
+            ar.replay_backward_f32(mem, ar.Searches(mem, {"q_pos": q_pos, "k_pos": kp, "cu": cu}), lq=wl.lq,
+                                   lk=len(kp), hq=wl.hq, hkv=wl.hkv, D=wl.d, causal=True, varlen=True,
+                                   n_seqs=len(cu) - 1)

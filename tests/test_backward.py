@@ -19,6 +19,13 @@ pytestmark = pytest.mark.gpu
 
 GRAD_TOL_MAX = 1e-2
 GRAD_TOL_RMS = 4e-3
+# float32 inputs: every step in float32 (unit roundoff 2^-24) with the exp2
+# unit's few-ulp error; the forward's LSE and O (and so D) carry errors of the
+# same relative order. Sums over at most a few thousand terms keep the error
+# near 1e-6 of the terms' size: the bar is 1e-4 of max|g_ref| and 2e-5 of its
+# root-mean-square.
+GRAD_TOL_MAX_F32 = 1e-4
+GRAD_TOL_RMS_F32 = 2e-5
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +42,7 @@ def orc():
     return oracle.get()
 
 
-def grad_compare(got, ref, what):
+def grad_compare(got, ref, what, tol_max=GRAD_TOL_MAX, tol_rms=GRAD_TOL_RMS):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -47,16 +54,15 @@ def grad_compare(got, ref, what):
     say("%s: max err %.3e of max %.3e (%.2e), rms err %.3e of rms %.3e (%.2e)" % (
         what, err, scale, err / scale if scale else 0.0, rms_err, rms_ref, rms_err / rms_ref if rms_ref else 0.0))
     record(what, elements=int(ref.size), max_abs_err=err, max_abs_ref=scale, rms_err=rms_err, rms_ref=rms_ref,
-           max_tol_rel=GRAD_TOL_MAX, rms_tol_rel=GRAD_TOL_RMS)
+           max_tol_rel=tol_max, rms_tol_rel=tol_rms)
     if scale == 0.0:
         # a reference that is zero by cancellation (one visible key: dP = D, so
         # dS = 0) comes out at float32 rounding level: D and dP are summed in
         # different orders; inputs here are of unit size
         assert err <= 1e-5, what + ": gradient must vanish"
         return
-    assert err <= GRAD_TOL_MAX * scale, "%s: max error %.3e > %.1e * %.3e" % (what, err, GRAD_TOL_MAX, scale)
-    assert rms_err <= GRAD_TOL_RMS * rms_ref, "%s: rms error %.3e > %.1e * %.3e" % (what, rms_err, GRAD_TOL_RMS,
-                                                                                   rms_ref)
+    assert err <= tol_max * scale, "%s: max error %.3e > %.1e * %.3e" % (what, err, tol_max, scale)
+    assert rms_err <= tol_rms * rms_ref, "%s: rms error %.3e > %.1e * %.3e" % (what, rms_err, tol_rms, rms_ref)
 
 
 def oracle_grads(orc, wl, rows=None, heads=None):
@@ -68,7 +74,8 @@ def oracle_grads(orc, wl, rows=None, heads=None):
     k = wl.kv_all("k")
     v = wl.kv_all("v")
     from synth import bf16_bits_to_f32
-    dout = bf16_bits_to_f32(wl.dout()).astype(np.float64)
+    dout = wl.dout()
+    dout = (dout if dout.dtype == np.float32 else bf16_bits_to_f32(dout)).astype(np.float64)
     dq, dk, dv, _ = orc.attention_grad(wl.q(), k, v, dout, qp, np.concatenate(kps), qs if docs is not None else None,
                                        True, rows=rows, heads=heads)
     if rows is not None:
@@ -299,3 +306,72 @@ def test_backward_empty_and_invisible_blocks(torch_cuda):
                        torch.empty((0, hq, d), device="cuda"), dk, dv)
     torch.cuda.synchronize()
     assert bool((dk == 0).all()) and bool((dv == 0).all())
+
+
+# ---------------------------------------------------------------------------
+# float32 inputs (the float32 kernels: every step in float32)
+
+def _f32_workloads():
+    from synth import WORKLOADS as W
+    return {w.name: w for w in [
+        W["zigzag1k_cp4_h1_d64_f32"],
+        W["zigzag64k_cp8_h32_d128"].scaled(name="zigzag2k_cp8_h4kv2_d128_f32", S=2048, hq=4, hkv=2, dtype="f32"),
+        W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs8k_zigzag_cp4_h2_d128_f32", S=8192, hq=2, hkv=2,
+                                                 docs=(256, 2048), dtype="f32"),
+        W["docs128k_zigzag_cp4_h32_d128"].scaled(name="docs4k_zigzag_cp4_h4kv1_d64_f32", S=4096, hq=4, hkv=1, d=64,
+                                                 sigma=1.0, docs=(128, 1024), dtype="f32"),
+    ]}
+
+
+@pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag2k_cp8_h4kv2_d128_f32",
+                                  "docs8k_zigzag_cp4_h2_d128_f32", "docs4k_zigzag_cp4_h4kv1_d64_f32"])
+def test_backward_float32_inputs(torch_cuda, orc, name):
+    """float32 q, k, v, dO (the 1K-token float32 workload, GQA and documents at
+    reduced sizes): the forward step and one gradient call per block, against
+    the oracle's gradients on every row and key."""
+    wl = _f32_workloads()[name]
+    say("backward float32 %s: S=%d cp=%d hq=%d hkv=%d d=%d blocks=%d" % (name, wl.S, wl.cp, wl.hq, wl.hkv, wl.d,
+                                                                          wl.n_blocks))
+    share, _, dq, dk, dv = _run(torch_cuda, wl)
+    assert share.q.dtype == torch_cuda.float32 and share.o.dtype == torch_cuda.float32
+    rdq, rdk, rdv = oracle_grads(orc, wl)
+    tol = dict(tol_max=GRAD_TOL_MAX_F32, tol_rms=GRAD_TOL_RMS_F32)
+    grad_compare(dq.cpu().numpy(), rdq, name + " dq", **tol)
+    grad_compare(np.concatenate([x.cpu().numpy() for x in dk]), np.concatenate(rdk), name + " dk", **tol)
+    grad_compare(np.concatenate([x.cpu().numpy() for x in dv]), np.concatenate(rdv), name + " dv", **tol)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lq,lk,hq,hkv", [(100, 77, 2, 1), (129, 200, 4, 4), (33, 1, 4, 2), (70, 130, 16, 1)])
+def test_backward_float32_ragged(torch_cuda, orc, d, causal, lq, lk, hq, hkv):
+    """float32 inputs at ragged sizes with random ascending positions, one
+    block: the forward, D and the gradients against the oracle."""
+    torch = torch_cuda
+    from context_long_sequence_amd import cpattn_bwd_delta, cpattn_partial, cpattn_partial_bwd
+    say("float32 ragged d=%d causal=%d lq=%d lk=%d hq=%d hkv=%d" % (d, causal, lq, lk, hq, hkv))
+    rng = np.random.default_rng(lq * 11 + lk + d + causal)
+    qp = np.sort(rng.choice(4 * (lq + lk), lq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(4 * (lq + lk), lk, replace=False)).astype(np.int32)
+
+    def rnd(shape, seed):
+        return torch.randn(shape, generator=torch.Generator().manual_seed(seed)) * 0.7
+    q, k, v, dout = rnd((lq, hq, d), 11), rnd((lk, hkv, d), 12), rnd((lk, hkv, d), 13), rnd((lq, hq, d), 14)
+    qg, kg, vg, dg = (x.cuda() for x in (q, k, v, dout))
+    qpd, kpd = torch.from_numpy(qp).cuda(), torch.from_numpy(kp).cuda()
+    o = torch.empty((lq, hq, d), device="cuda")
+    lse = torch.empty((hq, lq), device="cuda")
+    cpattn_partial(qg, kg, vg, qpd, kpd, o, lse, causal=causal)
+    delta = torch.empty((hq, lq), device="cuda")
+    cpattn_bwd_delta(o, dg, delta)
+    dq = torch.full((lq, hq, d), float("nan"), device="cuda")
+    dk = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    dv = torch.full((lk, hkv, d), float("nan"), device="cuda")
+    cpattn_partial_bwd(qg, kg, vg, dg, qpd, kpd, lse, delta, dq, dk, dv, causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _ = orc.attention_grad(q.numpy(), k.numpy(), v.numpy(), dout.numpy().astype(np.float64), qp, kp,
+                                          None, causal)
+    tol = dict(tol_max=GRAD_TOL_MAX_F32, tol_rms=GRAD_TOL_RMS_F32)
+    grad_compare(dq.cpu().numpy(), rdq, "float32 ragged dq", **tol)
+    grad_compare(dk.cpu().numpy(), rdk, "float32 ragged dk", **tol)
+    grad_compare(dv.cpu().numpy(), rdv, "float32 ragged dv", **tol)
