@@ -73,8 +73,9 @@ def record(what, **fields):
     import os
     path = os.environ.get("CPATTN_PARITY_LOG")
     if path:
+        node = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
         with open(path, "a") as f:
-            f.write(json.dumps(dict(test=what, **fields)) + "\n")
+            f.write(json.dumps(dict(test=what, node=node, **fields)) + "\n")
 
 
 def to_np(o, lse):
