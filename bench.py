@@ -308,6 +308,38 @@ def merge_bench(wl, steps, warmup, reps=10):
                                    "traffic": None, "bytes_per_launch": nbytes}}), flush=True)
 
 
+def bwd_call_bytes(q_pos, k_pos, cu, hq, hkv, d, esz, accumulate):
+    """Bytes one gradient call must move when each kernel reads what it uses
+    once: the key kernel reads K and V of the keys some row sees, Q and dO
+    (and LSE, D) of the rows that see some key, and writes dK and dV of every
+    key; the query kernel reads the same Q, dO, LSE, D, K and V and writes dQ
+    of the seeing rows (adding to it: reads it too), or of every row when it
+    is not accumulating. (Both kernels read Q, dO, K and V: the two-kernel
+    design forms S and dP in each instead of exchanging gradients through
+    atomics.)"""
+    q = np.asarray(q_pos, np.int64)
+    k = np.asarray(k_pos, np.int64)
+    lq, lk = len(q), len(k)
+    if lk == 0 or lq == 0:
+        rows = keys = 0
+    else:
+        lo_pos = np.full(lq, np.iinfo(np.int64).min) if cu is None else \
+            np.asarray(cu, np.int64)[np.searchsorted(cu, q, side="right") - 1]
+        lo = np.searchsorted(k, lo_pos, side="left")
+        hi = np.searchsorted(k, q, side="right")
+        seeing = hi > lo
+        rows = int(seeing.sum())
+        cover = np.zeros(lk + 1, np.int64)          # keys inside some row's visible range
+        np.add.at(cover, lo[seeing], 1)
+        np.add.at(cover, hi[seeing], -1)
+        keys = int((np.cumsum(cover)[:lk] > 0).sum())
+    qdo = 2 * rows * hq * d * esz + 2 * rows * hq * 4
+    kv = 2 * keys * hkv * d * esz
+    dkv = qdo + kv + 2 * lk * hkv * d * 4
+    dq = qdo + kv + (2 * rows * hq * d * 4 if accumulate else lq * hq * d * 4)
+    return dkv + dq
+
+
 def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None):
     """The gradient step of the share, timed: one cpattn_bwd_delta call, then
     one cpattn_partial_bwd call per block (its key kernel and query kernel).
@@ -348,6 +380,10 @@ def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None)
     torch.cuda.synchronize()
     call_ms = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_call)]))
     bwd_flops = 2.5 * step_flops
+    esz = 2 if wl.dtype == "bf16" else 4
+    call_bytes = float(np.mean([bwd_call_bytes(share.q_pos_host, share.k_pos_host[b], share.cu_host, wl.hq, wl.hkv,
+                                               wl.d, esz, i > 0) for i, b in enumerate(order)]))
+    traffic = profiled_traffic(wl.name, BWD_KERNEL_SOURCES, "traffic_bytes_per_block_call")
     tflops = bwd_flops / (ms * 1e-3) / 1e12
     call_flops = bwd_flops / len(order)
     achieved = call_flops / (call_ms * 1e-3) / 1e12
@@ -367,7 +403,9 @@ def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None)
                "peak": peak,
                "unit": "TFLOP/s",
                "frac": round(achieved / peak, 4),
-               "traffic": profiled_traffic(wl.name, BWD_KERNEL_SOURCES, "traffic_bytes_per_block_call"),
+               "traffic": traffic,
+               "algorithmic_bytes_per_call": round(call_bytes),
+               "traffic_over_algorithmic": round(traffic / call_bytes, 3) if traffic else None,
                "flop_per_call": call_flops,
                "mean_call_ms": round(call_ms, 5),
                "calls": n_call,

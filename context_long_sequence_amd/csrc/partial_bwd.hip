@@ -121,6 +121,53 @@ __device__ __forceinline__ void tr_offsets(int lane, int dt, int& a0, int& a8) {
   a8 = T::off(vr + 8, col >> 3) + ((col & 7) << 1);
 }
 
+// A wave's 32 rows of float32 results (lane l: row l % 32, head-dimension
+// entries 32dt + 8rr + 4(l/32) + 0..3 in acc[dt][4rr .. 4rr+3]), times mul,
+// written to rows row0 .. row0+31 of a float32 tensor (row_stride floats
+// apart, out pointing at the head's first column) through the LDS array
+// stg (32 rows x D/2 floats), so that every store instruction writes whole
+// 128-byte lines instead of 32 bytes of each of 32 rows: two passes of half
+// the head dimension, 16-byte chunks of row r XORed with r (mod the chunks
+// per row) against bank conflicts. Rows at or past n_valid are not written;
+// with `add` the stored values are added to.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(float* out, int64_t row_stride, int row0, int n_valid,
+                                               char CPATTN_LDS* stg, const f32x16_t* acc, float mul, bool add,
+                                               int lane) {
+  constexpr int DTP = D / 64;         // 32-column blocks per pass
+  constexpr int PCOLS = 32 * DTP;     // floats of a row per pass
+  constexpr int CHK = PCOLS / 4;      // 16-byte chunks of a row per pass
+  constexpr int RB = PCOLS * 4;       // staged row bytes
+  constexpr int RPI = 64 / CHK;       // rows per read
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 5, li = lane & 31;
+  const int rl = lane / CHK, cl = lane % CHK;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+    for (int dtp = 0; dtp < DTP; ++dtp)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x16_t& a = acc[ps * DTP + dtp];
+        const int c = 8 * dtp + 2 * rr + g;
+        *(f32x4 CPATTN_LDS*)(stg + li * RB + ((c ^ (li & (CHK - 1))) << 4)) =
+            f32x4{a[4 * rr] * mul, a[4 * rr + 1] * mul, a[4 * rr + 2] * mul, a[4 * rr + 3] * mul};
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int row = k * RPI + rl;
+      f32x4 v = *(const f32x4 CPATTN_LDS*)(stg + row * RB + ((cl ^ (row & (CHK - 1))) << 4));
+      if (row < n_valid) {
+        f32x4* dst = (f32x4*)(out + (int64_t)(row0 + row) * row_stride + ps * PCOLS + 4 * cl);
+        if (add) v += *dst;
+        *dst = v;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this pass's reads are done before the next one's writes
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Key kernel: dK and dV of 128 keys of one KV head.
 //
@@ -419,25 +466,16 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   }
 
   // ---- store: lane li holds key j0 + li, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
-  if (!key_valid) return;
-  float* dkrow = p.dk + ((int64_t)kj * p.hkv + hk) * D;
-  float* dvrow = p.dv + ((int64_t)kj * p.hkv + hk) * D;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d0 = 32 * dt + 8 * rr + 4 * g;
-      float4 a = make_float4(dk_acc[dt][4 * rr] * p.scale, dk_acc[dt][4 * rr + 1] * p.scale,
-                             dk_acc[dt][4 * rr + 2] * p.scale, dk_acc[dt][4 * rr + 3] * p.scale);
-      float4 b = make_float4(dv_acc[dt][4 * rr], dv_acc[dt][4 * rr + 1], dv_acc[dt][4 * rr + 2], dv_acc[dt][4 * rr + 3]);
-      if (p.acc_dkv) {
-        const float4 oa = *(const float4*)(dkrow + d0), ob = *(const float4*)(dvrow + d0);
-        a.x += oa.x; a.y += oa.y; a.z += oa.z; a.w += oa.w;
-        b.x += ob.x; b.y += ob.y; b.z += ob.z; b.w += ob.w;
-      }
-      *(float4*)(dkrow + d0) = a;
-      *(float4*)(dvrow + d0) = b;
-    }
+  // through the query stages, which no wave reads after the last barrier:
+  // consumer c stages dK in q_s[c] and dV in o_s[c]
+  const int n_keys = min(32, lk - j0);
+  if (n_keys <= 0) return;
+  const int cw = wave - 4;
+  const int64_t kv_row = (int64_t)p.hkv * D;
+  store_rows_lds<D>(p.dk + (int64_t)hk * D, kv_row, j0, n_keys, (char CPATTN_LDS*)q_s[cw], dk_acc, p.scale,
+                    p.acc_dkv != 0, lane);
+  store_rows_lds<D>(p.dv + (int64_t)hk * D, kv_row, j0, n_keys, (char CPATTN_LDS*)o_s[cw], dv_acc, 1.0f,
+                    p.acc_dkv != 0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,6 +501,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int r0 = wg_r0 + 32 * wave;
   const int qi = min(r0 + li, lq - 1);              // this lane's row (clamped)
   const bool row_valid = r0 + li < lq;
+  // Rows that see none of the block add nothing, and when accumulating dQ is
+  // left as it is: the common case (the block's first key is after the
+  // workgroup's last row) is decided by one load, before Q and dO are read.
+  if (p.acc_dq && (lk == 0 || (p.causal && p.k_pos[0] > p.q_pos[wg_r1 - 1]))) return;
 
   // the wave's rows: B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8_t qreg[NQ], dreg[NQ];
@@ -487,6 +529,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
     if constexpr (VARLEN) kb = wave_upper_bound(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
   }
   const int nt = ke > kb ? (ke - kb + 31) / 32 : 0;
+  // (with documents the rows may still see nothing)
+  if (nt == 0 && p.acc_dq) return;
 
   const int kv_stride = p.hkv * D * 2;
   const char* kbase = (const char*)p.k + (int64_t)hk * D * 2;
@@ -599,21 +643,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   }
 
   // ---- store: lane holds row qi, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
-  if (!row_valid) return;
-  float* dqrow = p.dq + ((int64_t)qi * p.hq + h) * D;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d0 = 32 * dt + 8 * rr + 4 * g;
-      float4 a = make_float4(acc[dt][4 * rr] * p.scale, acc[dt][4 * rr + 1] * p.scale, acc[dt][4 * rr + 2] * p.scale,
-                             acc[dt][4 * rr + 3] * p.scale);
-      if (p.acc_dq) {
-        const float4 o = *(const float4*)(dqrow + d0);
-        a.x += o.x; a.y += o.y; a.z += o.z; a.w += o.w;
-      }
-      *(float4*)(dqrow + d0) = a;
-    }
+  // through the K/V stages, which no wave reads after the last barrier: wave w
+  // stages its rows in stage array w
+  const int n_rows = min(32, lq - r0);
+  if (n_rows <= 0) return;
+  char CPATTN_LDS* stg = wave == 0 ? (char CPATTN_LDS*)k_s0 : wave == 1 ? (char CPATTN_LDS*)k_s1
+                       : wave == 2 ? (char CPATTN_LDS*)v_s0 : (char CPATTN_LDS*)v_s1;
+  store_rows_lds<D>(p.dq + (int64_t)h * D, (int64_t)p.hq * D, r0, n_rows, stg, acc, p.scale, p.acc_dq != 0, lane);
 }
 
 // ---------------------------------------------------------------------------

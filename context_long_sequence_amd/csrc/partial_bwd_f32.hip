@@ -262,6 +262,10 @@ __global__ __launch_bounds__(kF32Threads, 1) void bwd_dq_f32_kernel(BwdParams p)
   const int r0 = wg_r0 + 32 * wave;
   const int qi = min(r0 + li, lq - 1);  // this lane's row (clamped)
   const bool row_valid = r0 + li < lq;
+  // Rows that see none of the block add nothing, and when accumulating dQ is
+  // left as it is: the common case (the block's first key is after the
+  // workgroup's last row) is decided by one load, before Q and dO are read.
+  if (p.acc_dq && (lk == 0 || (p.causal && p.k_pos[0] > p.q_pos[wg_r1 - 1]))) return;
 
   // B operands of S^T = K Q^T and dP^T = V dO^T: the lane's row, columns 2ks + g
   float qreg[NK], dreg[NK];
@@ -287,6 +291,8 @@ __global__ __launch_bounds__(kF32Threads, 1) void bwd_dq_f32_kernel(BwdParams p)
     if constexpr (VARLEN) kb = wave_upper_bound(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
   }
   const int nt = ke > kb ? (ke - kb + 31) / 32 : 0;
+  // (with documents the rows may still see nothing)
+  if (nt == 0 && p.acc_dq) return;
 
   const int kv_stride = p.hkv * D * 4;
   const char* kbase = (const char*)p.k + (int64_t)hk * D * 4;

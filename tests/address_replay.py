@@ -534,6 +534,36 @@ def bwd_off(row, chunk, D):
     return row * 2 * D + ((chunk ^ swz) << 4)
 
 
+def staged_store_offsets(first_rows, n_rows, heads, head, D):
+    """Byte offsets of the 16-byte stores of store_rows_lds (partial_bwd.hip) for
+    waves whose first rows are first_rows [..., waves], into a float32
+    [n_rows][heads][D] tensor at head `head` (broadcast against first_rows);
+    LDS offsets checked against the 32 x D/2-float stage."""
+    dtp = D // 64
+    pcols = 32 * dtp
+    chk = pcols // 4
+    rb = pcols * 4
+    rpi = 64 // chk
+    li, g = LANES & 31, LANES >> 5
+    rl, cl = LANES // chk, LANES % chk
+    for dt in range(dtp):
+        for rr in range(4):
+            c = 8 * dt + 2 * rr + g
+            Mem.lds(li * rb + ((c ^ (li & (chk - 1))) << 4), 16, 32 * rb, "staged store write")
+    first = np.asarray(first_rows, np.int64)[..., None]
+    head = np.asarray(head, np.int64)[..., None]
+    n_valid = np.minimum(32, n_rows - first)
+    out = []
+    for ps in range(2):
+        for k in range(32 // rpi):
+            row = k * rpi + rl
+            Mem.lds(row * rb + ((cl ^ (row & (chk - 1))) << 4), 16, 32 * rb, "staged store read")
+            ok = np.broadcast_to(row < n_valid, np.broadcast(first, head, row).shape)
+            off = (((first + row) * heads + head) * D + ps * pcols + 4 * cl) * 4
+            out.append(np.broadcast_to(off, ok.shape)[ok])
+    return np.concatenate(out)
+
+
 def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False, acc_dkv=False):
     """One cpattn_partial_bwd call: the key kernel, then the query kernel.
     Tensors: 'q', 'dout', 'k', 'v', 'lse', 'delta', 'q_pos', 'k_pos', 'cu',
@@ -608,11 +638,10 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
             mem.index("k_pos", kj, "k_pos[kj]")
             if varlen:
                 sr.doc_end("cu", n_seqs, kpa[kj])
-        for dt in range(NDT):
-            for rr in range(4):
-                off = (((kj * hkv + hk3) * D + 32 * dt + 8 * rr + 4 * g) * 4)[key_valid]
-                mem.plain("dk", off, 16, "dk")
-                mem.plain("dv", off, 16, "dv")
+        # dK, dV leave through LDS (store_rows_lds): rows j0 + row, whole lines
+        off = staged_store_offsets(j0, lk, hkv, hk[:, None], D)
+        mem.plain("dk", off, 16, "dk")
+        mem.plain("dv", off, 16, "dv")
 
     # ---- query kernel: workgroup = 128 rows of one query head ----
     if lq > 0:
@@ -639,10 +668,6 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
             mem.index("q_pos", qi, "dq q_pos")
             if varlen:
                 sr.doc_start("cu", n_seqs, qp[qi])
-        for dt in range(NDT):
-            for rr in range(4):
-                off = (((qi * hq + h3) * D + 32 * dt + 8 * rr + 4 * g) * 4)[row_valid]
-                mem.plain("dq", off, 16, "dq")
         kb, ke = np.zeros(n_wg, np.int64), np.full(n_wg, lk, np.int64)
         if causal:
             mem.index("q_pos", np.stack([wg_r1 - 1, wg_r0]))
@@ -650,6 +675,10 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
             if varlen:
                 kb = sr.wave_upper_bound("k_pos", lk, sr.doc_start("cu", n_seqs, qp[wg_r0]) - 1)
         nt = np.where(ke > kb, (ke - kb + 31) // 32, 0)
+        if acc_dq and lk > 0 and causal:
+            mem.index("k_pos", [0], "k_pos[0]")
+        writes = ~((nt == 0) & bool(acc_dq))  # accumulating workgroups that see nothing leave dQ alone
+        mem.plain("dq", staged_store_offsets(r0[writes], lq, hq, h[writes][:, None], D), 16, "dq")
         ts, own = ragged_ranges(np.zeros(n_wg), nt)  # fetch(0), then fetch(t+1) for t + 1 < nt
         j0 = kb[own] + 32 * ts
         rows = clamp_rows(lk - j0, 32)
