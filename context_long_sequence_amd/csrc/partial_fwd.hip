@@ -634,8 +634,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     // call leaves the state exactly as it is (the merge weights would be 1
     // and 0), so the workgroup stops here; otherwise the block is skipped.
     // Keys all after the workgroup's last query is the common case, decided
-    // by one load before any search.
-    const bool none = p.causal && (lk == 0 || kpos[0] > p.q_pos[wg_r1 - 1]);
+    // by one load before any search (the block's last key, read with it,
+    // spares the searches below when the rows see the whole block).
+    const int32_t k_first = (p.causal && lk > 0) ? kpos[0] : 0;
+    const int32_t k_last = (p.causal && lk > 0) ? kpos[lk - 1] : 0;
+    const bool none = p.causal && (lk == 0 || k_first > p.q_pos[wg_r1 - 1]);
     if (none || lk <= 0) {
       if (!MULTI && p.accumulate) return;
       continue;
@@ -649,7 +652,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
 
     // ---- key range of the workgroup, and the per-wave fully visible range ----
     // (wave-cooperative searches: the positions are ascending, and a lower
-    // bound of x is the upper bound of x - 1; document starts are > INT32_MIN)
+    // bound of x is the upper bound of x - 1; document starts are > INT32_MIN).
+    // A search whose answer the block's first or last key already gives runs
+    // over an empty range: rows at or after the block's last key see all of
+    // it (the common case away from the diagonal), and a block whose first key
+    // is at or after a document start has no key before it.
     int kb = 0, ke = lk;
     f_lo = 0;
     f_hi = lk;
@@ -657,19 +664,21 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       // (an inactive wave, past the last row, searches with its workgroup's last row)
       const int32_t wq_hi = p.q_pos[wg_r1 - 1];
       const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi;
+      const bool all_wg = k_last <= wq_hi, all_wave = k_last <= q_lo;  // (q_lo <= wq_hi)
       if constexpr (VARLEN) {
         // both ends of both ranges in the same rounds (the document starts are known)
         int r[4];
         const int32_t* const ks[4] = {kpos, kpos, kpos, kpos};
-        const int ns[4] = {lk, lk, lk, lk};
+        const int ns[4] = {all_wg ? 0 : lk, all_wave ? 0 : lk, k_first >= s_wg ? 0 : lk, k_first >= s_wave ? 0 : lk};
         const int32_t xs[4] = {wq_hi, q_lo, s_wg - 1, s_wave - 1};
         wave_upper_bounds<4>(ks, ns, xs, r);
-        ke = r[0];
-        f_hi = r[1];
+        ke = all_wg ? lk : r[0];
+        f_hi = all_wave ? lk : r[1];
         kb = r[2];
         f_lo = r[3];
-      } else {
-        wave_upper_bound2(kpos, lk, wq_hi, q_lo, ke, f_hi);
+      } else if (!all_wave) {
+        if (all_wg) f_hi = wave_upper_bound(kpos, lk, q_lo);
+        else wave_upper_bound2(kpos, lk, wq_hi, q_lo, ke, f_hi);
       }
     }
     kt_begin = kb / BK;

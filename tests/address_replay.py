@@ -398,9 +398,10 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
         kbase = hk * D * c.esz
         alive = ~exited
         if causal and lk > 0:
-            mem.index(kp, [0], "kpos[0]")
+            mem.index(kp, [0, lk - 1], "kpos[0], kpos[lk - 1]")
             mem.index("q_pos", wg_r1 - 1)
             none = sr.arrays[kp][0] > qp[wg_r1 - 1]
+            k_first, k_last = int(sr.arrays[kp][0]), int(sr.arrays[kp][lk - 1])
         else:
             none = np.full(r0.shape, causal and lk == 0)
         skip = alive & (none | (lk <= 0))
@@ -443,11 +444,14 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
             wq_hi = qp[wg_r1 - 1].astype(np.int64)
             q_lo = qp[q_lo_i].astype(np.int64)
             ke, kb = ke.copy(), kb.copy()
-            ke[act] = sr.wave_upper_bound(kp, lk, wq_hi[act])
-            sr.wave_upper_bound(kp, lk, q_lo[act])
+            # searches whose answer the block's first or last key gives run over an empty range
+            s_ke = act & ~(k_last <= wq_hi)
+            ke[s_ke] = sr.wave_upper_bound(kp, lk, wq_hi[s_ke])
+            sr.wave_upper_bound(kp, lk, q_lo[act & ~(k_last <= q_lo)])
             if varlen:
-                kb[act] = sr.wave_upper_bound(kp, lk, s_wg[act] - 1)
-                sr.wave_upper_bound(kp, lk, s_wave[act] - 1)
+                s_kb = act & ~(k_first >= s_wg)
+                kb[s_kb] = sr.wave_upper_bound(kp, lk, s_wg[s_kb] - 1)
+                sr.wave_upper_bound(kp, lk, s_wave[act & ~(k_first >= s_wave)] - 1)
         kt_begin = kb // c.BK
         nt = (ke + c.BK - 1) // c.BK - kt_begin
         if not (np.all(kt_begin == kt_begin[:, :1]) and np.all(nt == nt[:, :1])):
