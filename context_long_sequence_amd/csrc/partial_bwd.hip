@@ -42,7 +42,9 @@
 //    keeps both the row reads (ds_read_b128, 16 rows at one chunk) and the
 //    transposed reads (4 rows x 4 chunks) free of bank conflicts.
 //  * Workgroup ids are remapped so that consecutive logical tiles run on
-//    one XCD (shared L2); the tiles with the most work go first.
+//    one XCD (shared L2) when the heads split evenly over the 8 XCDs (else
+//    the hardware's round-robin order spreads the heavy tiles); the tiles
+//    with the most work go first.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const bool producer = wave < 4;
   const int kw = wave & 3;                  // the wave's 32-key block
   const int g = lane >> 5, li = lane & 31;
-  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int L = tile_order(blockIdx.x, p.n_wg, p.hkv);
   const int hk = L / p.n_tiles;
   const int kt = L % p.n_tiles;  // early keys (seen by the most rows) first
   const int G = p.hq / p.hkv;
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, li = lane & 31;
-  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int L = tile_order(blockIdx.x, p.n_wg, p.hq);
   const int h = L / p.n_tiles;
   const int qt = p.n_tiles - 1 - L % p.n_tiles;  // late rows (that see the most keys) first
   const int hk = h / (p.hq / p.hkv);

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kF32Threads, 1) void bwd_dkv_f32_kernel(BwdParams p
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, li = lane & 31;
-  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int L = tile_order(blockIdx.x, p.n_wg, p.hkv);
   const int hk = L / p.n_tiles;
   const int kt = L % p.n_tiles;
   const int G = p.hq / p.hkv;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kF32Threads, 1) void bwd_dq_f32_kernel(BwdParams p)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, li = lane & 31;
-  const int L = xcd_remap(blockIdx.x, p.n_wg);
+  const int L = tile_order(blockIdx.x, p.n_wg, p.hq);
   const int h = L / p.n_tiles;
   const int qt = p.n_tiles - 1 - L % p.n_tiles;  // late rows (that see the most keys) first
   const int hk = h / (p.hq / p.hkv);

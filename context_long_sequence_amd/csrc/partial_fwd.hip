@@ -65,9 +65,11 @@
 //    the key-range bounds are found by the whole wave, 64 probes per round,
 //    the workgroup's and the wave's in the same rounds; and without
 //    documents Q and the first three tiles are requested before the searches.
-//  * Workgroup ids are remapped so that consecutive logical tiles (same KV
-//    head) run on the same XCD and share its L2; heavy (late-position) query
-//    tiles are scheduled first.
+//  * Heavy (late-position) query tiles are scheduled first. When the head
+//    groups split evenly over the 8 XCDs, workgroup ids are remapped so that
+//    consecutive logical tiles (same KV head) run on the same XCD and share
+//    its L2; otherwise the hardware's round-robin order is kept, so that no
+//    XCD gets all the heaviest tiles.
 //  * A multi-block call (several blocks that have all arrived) runs the same
 //    code in a loop over a table of blocks: each block gets its own
 //    emptiness test, searches and tile loop, while the running max, running
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int g = lane >> 5;                // half-wave
   const int li = lane & 31;               // query row within the wave
 
-  const int Lid = xcd_remap(blockIdx.x, p.n_wg);
+  const int Lid = tile_order(blockIdx.x, p.n_wg, p.n_hgroups);
   const int hgrp = Lid / p.n_qtiles;
   const int qt = p.n_qtiles - 1 - (Lid % p.n_qtiles);  // late (heavier) rows first
   const int hsub = wave % p.g_wg, rb = wave / p.g_wg;

@@ -56,6 +56,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + (x < rem ? x : rem) + slot;
 }
 
+// Logical tile of workgroup bid when the logical order is unit-major (a unit:
+// a head or head group, its tiles heaviest first). With a multiple of 8 units
+// each XCD gets whole units (xcd_remap: shared K/V in its L2, and every XCD
+// the same mix of heavy and light tiles). Otherwise contiguous ranges would
+// give one XCD all the heaviest tiles (two units of 4096 tiles: 1.75 times
+// the mean work), so the hardware's round-robin order is kept, which hands
+// every XCD every eighth tile of the heavy-first order.
+__device__ __forceinline__ int tile_order(int bid, int n, int units) {
+  return (units & 7) == 0 ? xcd_remap(bid, n) : bid;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   // raw buffer (stride 0): the record count is a byte count
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
