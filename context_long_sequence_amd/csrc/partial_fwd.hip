@@ -219,6 +219,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   };
 
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
+  // A single-block call's first and last key, read with the first loads (the
+  // emptiness test and the search shortcuts below use them).
+  const int32_t k_first0 = (!MULTI && p.causal && p.lk > 0) ? p.k_pos[0] : 0;
+  const int32_t k_last0 = (!MULTI && p.causal && p.lk > 0) ? p.k_pos[p.lk - 1] : 0;
   // Documents (the same for every block): the starts of the documents of the
   // workgroup's first row and of the wave's last row, and this lane's own. The
   // three document indices are searched together; when the wave's first and
@@ -638,8 +642,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     // Keys all after the workgroup's last query is the common case, decided
     // by one load before any search (the block's last key, read with it,
     // spares the searches below when the rows see the whole block).
-    const int32_t k_first = (p.causal && lk > 0) ? kpos[0] : 0;
-    const int32_t k_last = (p.causal && lk > 0) ? kpos[lk - 1] : 0;
+    const int32_t k_first = MULTI ? ((p.causal && lk > 0) ? kpos[0] : 0) : k_first0;
+    const int32_t k_last = MULTI ? ((p.causal && lk > 0) ? kpos[lk - 1] : 0) : k_last0;
     const bool none = p.causal && (lk == 0 || k_first > p.q_pos[wg_r1 - 1]);
     if (none || lk <= 0) {
       if (!MULTI && p.accumulate) return;

@@ -398,7 +398,7 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
         kbase = hk * D * c.esz
         alive = ~exited
         if causal and lk > 0:
-            mem.index(kp, [0, lk - 1], "kpos[0], kpos[lk - 1]")
+            mem.index(kp, [0, lk - 1], "kpos[0], kpos[lk - 1]")  # (a single-block call reads them first)
             mem.index("q_pos", wg_r1 - 1)
             none = sr.arrays[kp][0] > qp[wg_r1 - 1]
             k_first, k_last = int(sr.arrays[kp][0]), int(sr.arrays[kp][lk - 1])
