@@ -31,7 +31,8 @@
 //    registers, rounded to bf16, are directly the B operand of O^T = V^T P^T.
 //    O^T keeps each lane on one query row too, so the rescale is a per-lane
 //    scalar multiply. Q stays in registers for the whole call.
-//  * K and V tiles (64 keys) and the tile's key positions live in a ring of
+//  * K and V tiles (64 keys at d 128, 128 at d 64: the same bytes) and the
+//    tile's key positions live in a ring of
 //    four LDS stages, each its own LDS array. The first load groups go
 //    global -> LDS with buffer_load_dwordx4 ... lds; in steady state each
 //    iteration fetches the next group into registers (16-byte buffer loads
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   static_assert(NS == 4, "four LDS stages");
   __shared__ __attribute__((aligned(1024))) char k_s0[TB], k_s1[TB], k_s2[TB], k_s3[TB];
   __shared__ __attribute__((aligned(1024))) char v_s0[TB], v_s1[TB], v_s2[TB], v_s3[TB];
-  __shared__ __attribute__((aligned(16))) int32_t p_s0[64], p_s1[64], p_s2[64], p_s3[64];
+  __shared__ __attribute__((aligned(16))) int32_t p_s0[BK], p_s1[BK], p_s2[BK], p_s3[BK];
   auto kst = [&](auto st) __attribute__((always_inline)) -> char CPATTN_LDS* {
     constexpr int k = decltype(st)::value;
     if constexpr (k == 0) return (char CPATTN_LDS*)k_s0;
@@ -204,15 +205,15 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   auto load_first = [&](int kt0, int n_avail) __attribute__((always_inline)) {
     const int32_t* psrc = p.causal ? kpos : (const int32_t*)kraw;
     load_tile<TIn, D, false, kWaves>(kst(S0{}), kbase, kv_stride, kt0 * BK, lk, wave, lane, kvoff);
-    load_positions<kWaves>(pst(S0{}), psrc, kt0 * BK, lk, wave, lane);
+    load_positions<kWaves, BK>(pst(S0{}), psrc, kt0 * BK, lk, wave, lane);
     if (1 < n_avail) {
       load_tile<TIn, D, false, kWaves>(kst(S1{}), kbase, kv_stride, (kt0 + 1) * BK, lk, wave, lane, kvoff);
-      load_positions<kWaves>(pst(S1{}), psrc, (kt0 + 1) * BK, lk, wave, lane);
+      load_positions<kWaves, BK>(pst(S1{}), psrc, (kt0 + 1) * BK, lk, wave, lane);
     }
     load_tile<TIn, D, true, kWaves>(vst(S0{}), vbase, kv_stride, kt0 * BK, lk, wave, lane, vvoff);
     if (2 < n_avail) {
       load_tile<TIn, D, false, kWaves>(kst(S2{}), kbase, kv_stride, (kt0 + 2) * BK, lk, wave, lane, kvoff);
-      load_positions<kWaves>(pst(S2{}), psrc, (kt0 + 2) * BK, lk, wave, lane);
+      load_positions<kWaves, BK>(pst(S2{}), psrc, (kt0 + 2) * BK, lk, wave, lane);
     }
     if (1 < n_avail)
       load_tile<TIn, D, true, kWaves>(vst(S1{}), vbase, kv_stride, (kt0 + 1) * BK, lk, wave, lane, vvoff);
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // With d = 64 a tile's period is half as long, too short to cover the load
   // latency of a key range that streams from memory, and registers are to
   // spare: G(j) is then fetched two periods ahead into staging set j % 2.
-  constexpr bool kDeep = C::kBf16 && D == 64;
+  constexpr bool kDeep = false;
   constexpr int NSET = kDeep ? 2 : 1;
   u32x4_t kreg[NSET][C::kInst / kWaves], vreg[NSET][C::kInst / kWaves];
   int32_t preg[NSET] = {};
@@ -270,13 +271,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     const int j0 = (kt_begin + j) * BK;
     const int klim = (!kDeep || j + 1 < nt) ? lk : 0, vlim = (!kDeep || j < nt) ? lk : 0;
     fetch_tile<TIn, D, kWaves>(kreg[e], kbase, (int)kv_stride, j0 + BK, klim, wave, kvoff);
-    preg[e] = fetch_positions<kWaves>(p.causal ? kpos : nullptr, j0 + BK, klim, wave, lane);
+    preg[e] = fetch_positions<kWaves, BK>(p.causal ? kpos : nullptr, j0 + BK, klim, wave, lane);
     fetch_tile<TIn, D, kWaves>(vreg[e], vbase, (int)kv_stride, j0, vlim, wave, vvoff);
   };
   auto commit_group = [&](auto sk1, auto sv, auto set) __attribute__((always_inline)) {
     constexpr int e = decltype(set)::value;
     commit_tile<TIn, D, kWaves>(kst(sk1), kreg[e], wave, lane);
-    commit_positions<kWaves>(pst(sk1), preg[e], wave, lane);
+    commit_positions<kWaves, BK>(pst(sk1), preg[e], wave, lane);
     commit_tile<TIn, D, kWaves>(vst(sv), vreg[e], wave, lane);
   };
 
@@ -461,6 +462,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   auto mask = [&](const int32_t CPATTN_LDS* kp, int t) __attribute__((always_inline)) {
     const int lim = min(lk - (kt_begin + t) * BK, BK);  // keys of the tile inside the block
     const int go = 4 * g;
+    // (key go + jt + c < lim is tested as the constant jt + c < rem: held as
+    // a key index per register, the tests' operands take a register each)
+    const int rem = lim - go;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
         if (p.causal) kv = *(const i32x4 CPATTN_LDS*)(kp + go + jt);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          bool vis = go + jt + c < lim;
+          bool vis = jt + c < rem;
           if (p.causal) {
             vis = vis & (kv[c] <= my_qpos);
             if (VARLEN) vis = vis & (kv[c] >= my_start);
@@ -709,14 +713,17 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     // after its last tile, which its registers cannot otherwise afford)
     using More = std::false_type;
     using Last = std::true_type;
-    const int nmore = MULTI ? nt : nt - 1;
+    // (at d 64 the peeled copy of the step costs more registers than the
+    // stale scores it saves: every tile goes through the loop there as well)
+    constexpr bool kPeel = !MULTI && D != 64;
+    const int nmore = kPeel ? nt - 1 : nt;
     for (int t = 0; t < nmore; t += NS) {
       iteration(t, S0{}, More{});
       if (t + 1 < nmore) iteration(t + 1, S1{}, More{});
       if (t + 2 < nmore) iteration(t + 2, S2{}, More{});
       if (t + 3 < nmore) iteration(t + 3, S3{}, More{});
     }
-    if constexpr (!MULTI)
+    if constexpr (kPeel)
     switch (nmore & 3) {
       case 0: iteration(nmore, S0{}, Last{}); break;
       case 1: iteration(nmore, S1{}, Last{}); break;

@@ -15,7 +15,10 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 template <typename TIn, int D, int NW>
 struct Cfg {
   static constexpr bool kBf16 = sizeof(TIn) == 2;
-  static constexpr int kNB = kBf16 ? 2 : 1;           // 32-key blocks per tile
+  // 32-key blocks per tile: 64 keys at d 128; 128 at d 64, so that a tile has
+  // the bytes, MFMAs and registers of a d 128 one and the per-tile costs of
+  // the phases (barriers, fetch, commit, checks) are spread over twice the keys
+  static constexpr int kNB = kBf16 ? (D == 64 ? 4 : 2) : 1;
   static constexpr int kBK = 32 * kNB;                // keys per tile
   static constexpr int kRowBytes = D * (int)sizeof(TIn);
   static constexpr int kTileBytes = kBK * kRowBytes;
@@ -23,7 +26,7 @@ struct Cfg {
   static constexpr int kRowsPerInst = 1024 / kRowBytes;
   static constexpr int kNQ = kBf16 ? D / 16 : D / 2;  // Q operand registers (MFMA k-steps of S^T)
   static constexpr int kNDT = D / 32;                 // 32-column blocks of O^T
-  static constexpr int kPosPerWave = 64 / NW;         // key positions each wave stages
+  static constexpr int kPosPerWave = kBK / NW;        // key positions each wave stages
   static_assert(kInst % NW == 0, "tile must split evenly over the waves");
 
   // Swizzles (16-byte chunk index XOR row function). K is read as 16
@@ -122,15 +125,16 @@ __device__ __forceinline__ void load_tile(char CPATTN_LDS* lds_tile, const char*
   }
 }
 
-// Key positions of a tile: wave w loads entries [E*w, E*w+E), E = 64/NW, of
-// the 64-entry stage (the last valid position repeated past lk), one
-// instruction per wave. Without positions (non-causal calls) the same
-// instruction reads the key tensor instead, into a stage nobody reads.
-template <int NW>
+// Key positions of a tile of BK keys: wave w loads entries [E*w, E*w+E),
+// E = BK/NW, of the BK-entry stage (the last valid position repeated past
+// lk), one instruction per wave. Without positions (non-causal calls) the
+// same instruction reads the key tensor instead, into a stage nobody reads.
+template <int NW, int BK>
 __device__ __forceinline__ void load_positions(int32_t CPATTN_LDS* kp_tile, const int32_t* src, int r0, int lk,
                                                int wave, int lane) {
-  constexpr int E = 64 / NW;
-  const int rows = min(lk - r0, 64);
+  constexpr int E = BK / NW;
+  static_assert(E <= 64 && (E & (E - 1)) == 0, "a wave stages a power-of-two run of positions");
+  const int rows = min(lk - r0, BK);
   const int e = E * wave + (lane & (E - 1));
   const int idx = e < rows ? e : rows - 1;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + r0, rows * 4);
@@ -188,20 +192,20 @@ __device__ __forceinline__ void commit_tile(char CPATTN_LDS* lds_tile, const u32
     *(u32x4_t CPATTN_LDS*)(lds_tile + (wave + NW * it) * 1024 + lane * 16) = regs[it];
 }
 
-// Positions: lanes 0..E-1 of wave w (E = 64/NW) hold entries E*w.. (zero past
+// Positions: lanes 0..E-1 of wave w (E = BK/NW) hold entries E*w.. (zero past
 // the block, and everywhere when src is null: non-causal calls stage zeros
 // nobody reads).
-template <int NW>
+template <int NW, int BK>
 __device__ __forceinline__ int32_t fetch_positions(const int32_t* src, int r0, int lk, int wave, int lane) {
-  constexpr int E = 64 / NW;
-  const int rows = src ? clamp_rows(lk - r0, 64) : 0;
+  constexpr int E = BK / NW;
+  const int rows = src ? clamp_rows(lk - r0, BK) : 0;
   return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(src + r0, rows * 4),
                                                        (E * wave + (lane & (E - 1))) * 4, 0, 0);
 }
 
-template <int NW>
+template <int NW, int BK>
 __device__ __forceinline__ void commit_positions(int32_t CPATTN_LDS* kp_tile, int32_t v, int wave, int lane) {
-  constexpr int E = 64 / NW;
+  constexpr int E = BK / NW;
   if (lane < E) kp_tile[E * wave + lane] = v;
 }
 

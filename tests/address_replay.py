@@ -243,7 +243,7 @@ class FwdCfg:
         self.bf16 = in_bf16
         self.D = D
         self.esz = 2 if in_bf16 else 4
-        self.NB = 2 if in_bf16 else 1
+        self.NB = (4 if D == 64 else 2) if in_bf16 else 1
         self.BK = 32 * self.NB
         self.row_bytes = D * self.esz
         self.tile_bytes = self.BK * self.row_bytes
@@ -299,17 +299,17 @@ def load_tile(mem, c, tensor, head_base, row_stride, r0, lk, wave, is_v):
                        "load_tile (tail)")
 
 
-def load_positions(mem, src, r0, lk, wave):
-    E = 64 // FwdCfg.NW
+def load_positions(mem, src, r0, lk, wave, BK=64):
+    E = BK // FwdCfg.NW
     r0 = np.atleast_1d(np.asarray(r0, np.int64))
-    rows = np.minimum(lk - r0, 64)
+    rows = np.minimum(lk - r0, BK)
     if r0.size and rows.min() <= 0:
         raise AccessError("load_positions asked for positions at or past the block's end")
     issuing = LANES[LANES < E]  # the load sits under `lane < E`
     e = E * wave + (issuing & (E - 1))
     idx = np.where(e < rows[:, None], e, rows[:, None] - 1)
     mem.buffer(src, r0 * 4, rows * 4, idx * 4, 4, "load_positions")
-    mem.lds(E * wave * 4 + issuing * 4, 4, 64 * 4, "load_positions")
+    mem.lds(E * wave * 4 + issuing * 4, 4, BK * 4, "load_positions")
 
 
 def fetch_tiles(mem, c, tensor, head_base, row_stride, r0s, lims, wave, is_v):
@@ -323,13 +323,13 @@ def fetch_tiles(mem, c, tensor, head_base, row_stride, r0s, lims, wave, is_v):
         mem.lds((wave + c.NW * it) * 1024 + LANES * 16, 16, c.tile_bytes, "commit_tile")
 
 
-def fetch_positions(mem, src, r0s, lims, wave):
-    E = 64 // FwdCfg.NW
+def fetch_positions(mem, src, r0s, lims, wave, BK=64):
+    E = BK // FwdCfg.NW
     r0s = np.asarray(r0s, np.int64)
     if src is None:  # null source: an empty range
         rows, src = np.zeros_like(r0s), "null"
     else:
-        rows = clamp_rows(np.asarray(lims, np.int64) - r0s, 64)
+        rows = clamp_rows(np.asarray(lims, np.int64) - r0s, BK)
     mem.buffer(src, r0s * 4, rows * 4, (E * wave + (LANES & (E - 1))) * 4, 4, "fetch_positions")
 
 
@@ -350,7 +350,7 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
     if n_wg <= 0:
         return 0
     check_remap(n_wg)
-    deep = in_bf16 and D == 64
+    deep = False  # (two-ahead staging sets are no longer used)
     osz = 2 if out_bf16 else 4
     row_stride = hkv * D * c.esz
     li, g = LANES & 31, LANES >> 5
@@ -424,13 +424,13 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
                     continue
                 t0, na, hb = kt0[m], n_avail[m], kbase[m]
                 load_tile(mem, c, kt, hb, row_stride, t0 * c.BK, lk, wv, False)
-                load_positions(mem, psrc, t0 * c.BK, lk, wv)
+                load_positions(mem, psrc, t0 * c.BK, lk, wv, c.BK)
                 m1, m2 = na > 1, na > 2
                 load_tile(mem, c, kt, hb[m1], row_stride, (t0[m1] + 1) * c.BK, lk, wv, False)
-                load_positions(mem, psrc, (t0[m1] + 1) * c.BK, lk, wv)
+                load_positions(mem, psrc, (t0[m1] + 1) * c.BK, lk, wv, c.BK)
                 load_tile(mem, c, vt, hb, row_stride, t0 * c.BK, lk, wv, True)
                 load_tile(mem, c, kt, hb[m2], row_stride, (t0[m2] + 2) * c.BK, lk, wv, False)
-                load_positions(mem, psrc, (t0[m2] + 2) * c.BK, lk, wv)
+                load_positions(mem, psrc, (t0[m2] + 2) * c.BK, lk, wv, c.BK)
                 load_tile(mem, c, vt, hb[m1], row_stride, (t0[m1] + 1) * c.BK, lk, wv, True)
 
         early = not varlen
@@ -478,7 +478,7 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
                 klim = vlim = np.full(js.shape, lk)
             j0 = (kb_e[own] + js) * c.BK
             fetch_tiles(mem, c, kt, hb_e[own], row_stride, j0 + c.BK, klim, wv, False)
-            fetch_positions(mem, kp if causal else None, j0 + c.BK, klim, wv)
+            fetch_positions(mem, kp if causal else None, j0 + c.BK, klim, wv, c.BK)
             fetch_tiles(mem, c, vt, hb_e[own], row_stride, j0, vlim, wv, True)
 
     # epilogue (workgroups that left early, and accumulating ones that saw nothing, write nothing)

@@ -161,7 +161,7 @@ def test_checks_catch_a_tile_past_the_block():
     with pytest.raises(ar.AccessError):
         ar.load_tile(mem, c, "k", 0, row_stride, 320, lk, 0, False)
     with pytest.raises(ar.AccessError):
-        ar.load_positions(mem, "kp", 320, lk, 0)
+        ar.load_positions(mem, "kp", 320, lk, 0, c.BK)
     with pytest.raises(ar.AccessError):
         mem.buffer("k", np.array([256 * row_stride]), np.array([45 * row_stride]),
                         ar.LANES * 16 + 44 * row_stride, 16)
