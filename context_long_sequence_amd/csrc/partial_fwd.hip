@@ -487,7 +487,12 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // Raise the running max where tile t's max exceeds it by more than kTau
   // (base 2), rescaling the running sum and O accordingly.
   auto raise_max = [&]() __attribute__((always_inline)) {
+    // (opaque start: the two passes would otherwise share one max, which the
+    // compiler then forms ahead of the rare branch on every tile. With
+    // documents the max is needed often, at every row's document start, and
+    // the shared max measured faster there.)
     float mx = neg_inf();
+    if constexpr (!VARLEN) pin(mx);
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
