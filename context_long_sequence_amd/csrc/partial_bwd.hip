@@ -355,14 +355,27 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       q4 = p.causal ? *(const i32x4 CPATTN_LDS*)((const int32_t CPATTN_LDS*)p_s[st] + 8 * rr + 4 * g)
                     : i32x4{0, 0, 0, 0};
     };
-    auto softmax_rr = [&](const f32x16_t& s, const f32x16_t& dp, int rr) __attribute__((always_inline)) {
+    // Without documents, a query tile whose first row is at or after the
+    // wave's last key sees all of the wave's keys (rows past the end have
+    // LSE +inf, so P = 0): no mask then.
+    const int32_t wave_klast = __builtin_amdgcn_readfirstlane(p.causal ? p.k_pos[min(j0 + 31, lk - 1)] : 0);
+    const bool keys_full = j0 + 32 <= lk;
+    auto tile_full = [&](int st) __attribute__((always_inline)) {
+      return keys_full &&
+             (!p.causal || (!VARLEN && __builtin_amdgcn_readfirstlane(p_s[st][0]) >= wave_klast));
+    };
+    auto softmax_rr = [&](const f32x16_t& s, const f32x16_t& dp, int rr, auto masked) __attribute__((always_inline)) {
+      constexpr bool M = decltype(masked)::value;
       float pv[4], dv[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        bool vis = key_valid;
-        if (p.causal) {
-          vis = vis & (q4[c] >= my_kpos);
-          if (VARLEN) vis = vis & (q4[c] < my_kend);
+        bool vis = true;
+        if constexpr (M) {
+          vis = key_valid;
+          if (p.causal) {
+            vis = vis & (q4[c] >= my_kpos);
+            if (VARLEN) vis = vis & (q4[c] < my_kend);
+          }
         }
         pv[c] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -l4[c])) : 0.f;
         dv[c] = pv[c] * (dp[4 * rr + c] - d4[c]);
@@ -384,13 +397,18 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       (void)cs;
       if (k < n_it) {
         const int st1 = (st + 1) & (NS - 1);
+        const bool full = tile_full(st);
+        auto soft = [&](int rr) __attribute__((always_inline)) {
+          if (full) softmax_rr(s_c, dp_c, rr, std::false_type{});
+          else softmax_rr(s_c, dp_c, rr, std::true_type{});
+        };
         if (k + 1 < n_it) {
           constexpr int SP = NQ / 2;  // MFMAs per slice
           static_assert(SP >= 2, "a slice's row reads go one MFMA ahead of it");
           f32x16_t s_n, dp_n;
           sdp(st1, s_n, dp_n, [&](int m) __attribute__((always_inline)) {
             if (m % SP == SP - 2) read_rows(st, m / SP);
-            if (m % SP == SP - 1) softmax_rr(s_c, dp_c, m / SP);
+            if (m % SP == SP - 1) soft(m / SP);
           });
           s_c = s_n;
           dp_c = dp_n;
@@ -398,7 +416,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             read_rows(st, rr);
-            softmax_rr(s_c, dp_c, rr);
+            soft(rr);
           }
         }
         char CPATTN_LDS* xb = (char CPATTN_LDS*)x_s[k & 1][kw] + 16 * lane;
@@ -523,6 +541,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const float dlt = row_valid ? p.delta[(int64_t)h * lq + qi] : 0.f;
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
   const int32_t my_start = VARLEN ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
+  const int32_t wq_first = __builtin_amdgcn_readfirstlane(p.causal ? p.q_pos[min(r0, lq - 1)] : 0);  // rows ascend
 
   // keys the workgroup's rows can see
   int kb = 0, ke = lk;
@@ -597,28 +616,40 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
 
-    // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile
+    // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile.
+    // Without documents, a tile of 32 keys inside the block that are all at
+    // or before the wave's first row is seen in full by every row of the wave
+    // (rows past the end have LSE +inf, so P = 0): no mask.
     const int lim = min(lk - (kb + 32 * t), 32);
+    const bool full = lim == 32 && (!p.causal || (!VARLEN && __builtin_amdgcn_readfirstlane(pl[31]) <= wq_first));
     uint32_t pd[8];
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    auto dsoft = [&](auto masked) __attribute__((always_inline)) {
+      constexpr bool M = decltype(masked)::value;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      i32x4 k4 = {0, 0, 0, 0};
-      if (p.causal) k4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
-      float dv[4];
+      for (int rr = 0; rr < 4; ++rr) {
+        i32x4 k4 = {0, 0, 0, 0};
+        if (M && p.causal) k4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
+        float dv[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bool vis = 8 * rr + 4 * g + c < lim;
-        if (p.causal) {
-          vis = vis & (k4[c] <= my_qpos);
-          if (VARLEN) vis = vis & (k4[c] >= my_start);
+        for (int c = 0; c < 4; ++c) {
+          bool vis = true;
+          if constexpr (M) {
+            vis = 8 * rr + 4 * g + c < lim;
+            if (p.causal) {
+              vis = vis & (k4[c] <= my_qpos);
+              if (VARLEN) vis = vis & (k4[c] >= my_start);
+            }
+          }
+          const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -lse2)) : 0.f;
+          dv[c] = pv * (dp[4 * rr + c] - dlt);
         }
-        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -lse2)) : 0.f;
-        dv[c] = pv * (dp[4 * rr + c] - dlt);
+        pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+        pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
       }
-      pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
-      pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
-    }
+    };
+    if (full) dsoft(std::false_type{});
+    else dsoft(std::true_type{});
 
     // dQ^T += K^T dS^T (K^T read transposed, RING ahead)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -640,6 +640,7 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
             mem.plain("v", off, 16, "dkv vreg")
         if causal:
             mem.index("k_pos", kj, "k_pos[kj]")
+            mem.index("k_pos", np.minimum(j0 + 31, lk - 1), "dkv wave's last key")
             if varlen:
                 sr.doc_end("cu", n_seqs, kpa[kj])
         # dK, dV leave through LDS (store_rows_lds): rows j0 + row, whole lines
@@ -670,6 +671,7 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
         mem.index("delta", (h3 * lq + qi)[row_valid], "dq delta")
         if causal:
             mem.index("q_pos", qi, "dq q_pos")
+            mem.index("q_pos", np.minimum(r0, lq - 1), "dq wave's first row")
             if varlen:
                 sr.doc_start("cu", n_seqs, qp[qi])
         kb, ke = np.zeros(n_wg, np.int64), np.full(n_wg, lk, np.int64)
@@ -795,6 +797,7 @@ def replay_backward_f32(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_
         mem.index("delta", (h3 * lq + qi)[row_valid], "dq delta")
         if causal:
             mem.index("q_pos", qi, "dq q_pos")
+            mem.index("q_pos", np.minimum(r0, lq - 1), "dq wave's first row")
             if varlen:
                 sr.doc_start("cu", n_seqs, qp[qi])
         for dt in range(NDT):
