@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   constexpr int U = TB / 16;                // 16-byte units of one tile
   constexpr int FT = kDkvThreads / 2;       // the consumer waves move the query tiles
   constexpr int NU = 2 * U / FT;            // units of the (Q, dO) pair per consumer thread
-  static_assert(NU >= 1 && (2 * U) % FT == 0, "the pair of tiles splits evenly over the consumer threads");
+  static_assert(NU >= 1 && U % FT == 0, "each tile splits evenly over the consumer threads");
   __shared__ __attribute__((aligned(1024))) char q_s[NS][TB], o_s[NS][TB];
   __shared__ __attribute__((aligned(1024))) char x_s[2][4][4][1024];  // [buffer][key block][part][lane]
   __shared__ __attribute__((aligned(16))) float l_s[NS][32], d_s[NS][32];
@@ -255,9 +255,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     const int rows = clamp_rows(lq - i0, 32);          // 0 past the last tile: nothing is read
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = ct + FT * u;
-      const bool is_o = unit >= U;                     // wave-uniform
-      const int lu = is_o ? unit - U : unit;
+      // (0 <= ct < FT and FT divides U: the tile of unit ct + FT u is known
+      // from u alone, so the buffer base is scalar)
+      const bool is_o = FT * u >= U;
+      const int lu = ct + FT * u - (is_o ? U : 0);
       const char* base = (const char*)(is_o ? p.dout : p.q) + (int64_t)hh * D * 2 + (int64_t)i0 * q_stride;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (int64_t)rows * q_stride);
       xr[e][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lu / T::kChunks) * q_stride + (lu % T::kChunks) * 16,
@@ -278,9 +279,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     constexpr int e = decltype(set)::value;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = ct + FT * u;
-      const bool is_o = unit >= U;
-      const int lu = is_o ? unit - U : unit;
+      const bool is_o = FT * u >= U;
+      const int lu = ct + FT * u - (is_o ? U : 0);
       char CPATTN_LDS* tile = (char CPATTN_LDS*)(is_o ? o_s[st] : q_s[st]);
       *(u32x4_t CPATTN_LDS*)(tile + T::off(lu / T::kChunks, lu % T::kChunks)) = xr[e][u];
     }
@@ -585,6 +585,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
     fetch(0);
     commit(0);
   }
+  // (likewise before the loop: the Q and dO loads are done once the first
+  // tile is committed, and with no tile the loop does not run)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   phase_barrier();
   for (int t = 0; t < nt; ++t) {
     const int st = t & 1;
@@ -672,6 +675,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
     if (t + 1 < nt) commit(st ^ 1);
+    // Nothing is in flight here (the commit waited for its loads). Saying so
+    // keeps the compiler's wait analysis exact across the conditional commit:
+    // otherwise it takes the skipped commit's loads as possibly pending and
+    // waits in the next tile's matrix products for the tile fetch just
+    // issued.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
   }
 
