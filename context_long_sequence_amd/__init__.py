@@ -69,6 +69,13 @@ def load_library(path=LIB_PATH):
     lib.cpattn_varlen_partial.restype = ctypes.c_int
     lib.cpattn_varlen_partial.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32, f32,
                                           vp, ctypes.c_int, vp, i32, vp]
+    lib.cpattn_partial_workgroups.restype = ctypes.c_int64
+    lib.cpattn_partial_workgroups.argtypes = [i64, i32, i32]
+    lib.cpattn_varlen_plan.restype = ctypes.c_int
+    lib.cpattn_varlen_plan.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, i32, ctypes.c_int, vp, i64]
+    lib.cpattn_varlen_partial_ordered.restype = ctypes.c_int
+    lib.cpattn_varlen_partial_ordered.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32,
+                                                  f32, vp, ctypes.c_int, vp, i32, vp, i64, vp]
     lib.cpattn_partial_multi.restype = ctypes.c_int
     lib.cpattn_partial_multi.argtypes = [vp, vp, vp, ctypes.c_int, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32,
                                          i32, f32, vp, ctypes.c_int, vp, i32, vp]
@@ -87,7 +94,7 @@ def load_library(path=LIB_PATH):
 def header_functions(path=HEADER):
     """Names of the functions declared in include/cpattn.h."""
     text = open(path).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(cpattn_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(cpattn_[a-z_]+)\s*\(", text, re.M)))
 
 
 def _check(lib, status):
@@ -178,8 +185,10 @@ def cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0
 
 
 def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_scale=0.0, accumulate=False,
-                          stream=None):
-    """As cpattn_partial, causal within documents given by device cu_seqlens."""
+                          stream=None, wg_order=None):
+    """As cpattn_partial, causal within documents given by device cu_seqlens.
+    wg_order (optional int32 device tensor, from cpattn_varlen_plan): the
+    dispatch order (cpattn_varlen_partial_ordered)."""
     import torch
     lib = load_library()
     lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
@@ -189,12 +198,42 @@ def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_sca
     _pos_len(k_pos, lk, "k_pos")
     if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise CpattnError(2, "cu_seqlens must be 1-D with n_seqs + 1 >= 2 entries")
-    st = lib.cpattn_varlen_partial(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq,
-                                   lk, hq, hkv, d, _dev(q_pos, "q_pos", torch.int32),
-                                   _dev(k_pos, "k_pos", torch.int32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
-                                   cu_seqlens.numel() - 1, float(softmax_scale), _dev(o, "o"), _dtype_code(o),
-                                   _dev(lse, "lse", torch.float32), int(bool(accumulate)), _stream(stream))
+    args = [_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dtype_code(q), lq, lk, hq, hkv, d,
+            _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32), cu_seqlens.numel() - 1, float(softmax_scale), _dev(o, "o"),
+            _dtype_code(o), _dev(lse, "lse", torch.float32), int(bool(accumulate))]
+    if wg_order is None:
+        st = lib.cpattn_varlen_partial(*args, _stream(stream))
+    else:
+        if wg_order.dim() != 1:
+            raise CpattnError(2, "wg_order must be 1-D")
+        st = lib.cpattn_varlen_partial_ordered(*args, _dev(wg_order, "wg_order", torch.int32), wg_order.numel(),
+                                               _stream(stream))
     _check(lib, st)
+
+
+def cpattn_partial_workgroups(lq, hq, hkv):
+    """Workgroups of one cpattn_partial / cpattn_varlen_partial call (-1 for invalid sizes)."""
+    return int(load_library().cpattn_partial_workgroups(int(lq), int(hq), int(hkv)))
+
+
+def cpattn_varlen_plan(q_pos, k_pos, cu_seqlens, hq, hkv, head_dim, in_dtype="bf16"):
+    """Dispatch order for cpattn_varlen_partial(..., wg_order=) from HOST
+    positions and document offsets (numpy int32): an int32 numpy array."""
+    lib = load_library()
+    qp = np.ascontiguousarray(q_pos, np.int32)
+    kp = np.ascontiguousarray(k_pos, np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    n = cpattn_partial_workgroups(len(qp), hq, hkv)
+    if n < 0:
+        raise CpattnError(2, "invalid sizes lq=%d hq=%d hkv=%d" % (len(qp), hq, hkv))
+    order = np.zeros(max(n, 1), np.int32)
+    code = in_dtype if isinstance(in_dtype, int) else (CPATTN_BF16 if in_dtype == "bf16" else CPATTN_F32)
+    st = lib.cpattn_varlen_plan(qp.ctypes.data, len(qp), kp.ctypes.data if len(kp) else None, len(kp),
+                                cu.ctypes.data, len(cu) - 1, int(hq), int(hkv), int(head_dim), code,
+                                order.ctypes.data, n)
+    _check(lib, st)
+    return order[:n]
 
 
 def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,
@@ -298,5 +337,6 @@ def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, caus
 
 
 __all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_partial_multi",
+           "cpattn_partial_workgroups", "cpattn_varlen_plan",
            "cpattn_merge_lse", "cpattn_bwd_delta", "cpattn_partial_bwd", "cpattn_version",
            "CpattnError", "load_library", "header_functions"]

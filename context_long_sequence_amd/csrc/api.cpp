@@ -62,6 +62,24 @@ cpattn_status check_sorted_device(const int32_t* dptr, int64_t n, const char* na
   return CPATTN_OK;
 }
 
+// Optional O(n) check that a device dispatch order is a permutation of [0, n)
+// (synchronises `stream`).
+cpattn_status check_permutation_device(const int32_t* dptr, int64_t n, hipStream_t stream) {
+  std::vector<int32_t> h((size_t)n);
+  hipError_t e = hipMemcpyAsync(h.data(), dptr, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "reading wg_order for validation: %s", hipGetErrorString(e));
+  std::vector<char> seen((size_t)n, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t x = h[(size_t)i];
+    if (x < 0 || x >= n || seen[(size_t)x])
+      return fail(CPATTN_ERR_RANGE, "wg_order is not a permutation of [0, %lld): entry %lld is %d", (long long)n,
+                  (long long)i, x);
+    seen[(size_t)x] = 1;
+  }
+  return CPATTN_OK;
+}
+
 size_t dsize(cpattn_dtype t) { return t == CPATTN_BF16 ? 2 : 4; }
 
 cpattn_status check_partial_args(const void* q, const void* k, const void* v, cpattn_dtype in_dtype, int64_t lq,
@@ -106,12 +124,13 @@ cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpatt
                               int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
                               const int32_t* k_pos, const int32_t* cu_seqlens, int32_t n_seqs, int32_t causal,
                               float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse, int32_t accumulate,
-                              void* stream) {
+                              void* stream, const int32_t* wg_order = nullptr) {
   hipStream_t s = (hipStream_t)stream;
   if (validate_env() && causal) {
     cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
     if (st == CPATTN_OK) st = check_sorted_device(k_pos, lk, "k_pos", s);
     if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
+    if (st == CPATTN_OK && wg_order) st = check_permutation_device(wg_order, cpattn::partial_workgroups(lq, hq, hkv), s);
     if (st != CPATTN_OK) return st;
   }
   if (lq == 0) return ok();
@@ -122,6 +141,7 @@ cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpatt
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal; p.accumulate = accumulate;
+  p.wg_order = wg_order;
   hipError_t e = cpattn::launch_partial(p, in_dtype == CPATTN_BF16, o_dtype == CPATTN_BF16, head_dim,
                                         cu_seqlens != nullptr, s);
   if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -249,6 +269,61 @@ cpattn_status cpattn_varlen_partial(const void* q, const void* k, const void* v,
   if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
   return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, cu_seqlens, n_seqs, 1,
                          softmax_scale, o, o_dtype, lse, accumulate, stream);
+}
+
+int64_t cpattn_partial_workgroups(int64_t lq, int32_t hq, int32_t hkv) {
+  if (lq < 0 || hq < 1 || hkv < 1 || hq % hkv != 0) return -1;
+  return cpattn::partial_workgroups(lq, hq, hkv);
+}
+
+cpattn_status cpattn_varlen_plan(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                 int32_t head_dim, cpattn_dtype in_dtype, int32_t* order, int64_t n_order) {
+  if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
+  if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(CPATTN_ERR_SHAPE, "hq must be a positive multiple of hkv (hq=%d, hkv=%d)", hq, hkv);
+  if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
+  if (in_dtype != CPATTN_BF16 && in_dtype != CPATTN_F32) return fail(CPATTN_ERR_DTYPE, "in_dtype must be bf16 or float32");
+  if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv);
+  if (n_order != n) return fail(CPATTN_ERR_SHAPE, "n_order must be %lld (the call's workgroups), got %lld",
+                                (long long)n, (long long)n_order);
+  if (n == 0) return ok();
+  if (!q_pos || !cu_seqlens || !order || (lk > 0 && !k_pos))
+    return fail(CPATTN_ERR_NULL, "q_pos, k_pos, cu_seqlens and order must be non-NULL");
+  for (int64_t i = 1; i < lq; ++i)
+    if (q_pos[i] < q_pos[i - 1]) return fail(CPATTN_ERR_UNSORTED, "q_pos is not ascending at index %lld", (long long)i);
+  for (int64_t i = 1; i < lk; ++i)
+    if (k_pos[i] < k_pos[i - 1]) return fail(CPATTN_ERR_UNSORTED, "k_pos is not ascending at index %lld", (long long)i);
+  for (int32_t i = 1; i <= n_seqs; ++i)
+    if (cu_seqlens[i] < cu_seqlens[i - 1])
+      return fail(CPATTN_ERR_UNSORTED, "cu_seqlens is not ascending at index %d", i);
+  cpattn::plan_varlen_order(q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, hkv, in_dtype == CPATTN_BF16, head_dim,
+                            order);
+  return ok();
+}
+
+cpattn_status cpattn_varlen_partial_ordered(const void* q, const void* k, const void* v, cpattn_dtype in_dtype,
+                                            int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                            const int32_t* q_pos, const int32_t* k_pos, const int32_t* cu_seqlens,
+                                            int32_t n_seqs, float softmax_scale, void* o, cpattn_dtype o_dtype,
+                                            float* lse, int32_t accumulate, const int32_t* wg_order,
+                                            int64_t n_order, void* stream) {
+  cpattn_status st = check_partial_args(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, 1, o, o_dtype,
+                                        lse, accumulate);
+  if (st != CPATTN_OK) return st;
+  if (!cu_seqlens) return fail(CPATTN_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
+  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv);
+  if (n_order != n) return fail(CPATTN_ERR_SHAPE, "n_order must be %lld (the call's workgroups), got %lld",
+                                (long long)n, (long long)n_order);
+  if (n > 0 && !wg_order) return fail(CPATTN_ERR_NULL, "wg_order must be non-NULL");
+  if (!aligned(wg_order, 4)) return fail(CPATTN_ERR_ALIGN, "wg_order must be 4-byte aligned");
+  return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, cu_seqlens, n_seqs, 1,
+                         softmax_scale, o, o_dtype, lse, accumulate, stream, n > 0 ? wg_order : nullptr);
 }
 
 cpattn_status cpattn_partial_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,

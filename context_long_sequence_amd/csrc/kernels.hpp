@@ -23,6 +23,7 @@ struct PartialParams {
   int32_t n_qtiles, n_hgroups, n_wg;
   float scale_log2;           // softmax scale * log2(e)
   int32_t causal, accumulate;
+  const int32_t* wg_order;    // optional dispatch order: logical tile of each workgroup id (else tile_order)
 };
 
 // The KV blocks of a multi-block call (passed by value as a kernel argument).
@@ -41,6 +42,15 @@ hipError_t launch_partial(PartialParams p, int in_bf16, int out_bf16, int head_d
 // Enqueue the kernel over the blocks of `bt` in order (p's k, v, k_pos, lk unused).
 hipError_t launch_partial_multi(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
                                 bool varlen, hipStream_t stream);
+
+// Workgroups of a single-block call (the length of a dispatch order).
+int64_t partial_workgroups(int64_t lq, int32_t hq, int32_t hkv);
+
+// Host: a dispatch order for a single-block call with documents (all
+// arguments in host memory, already validated): within each XCD's set of
+// logical tiles, the tiles that load the most key tiles go first.
+void plan_varlen_order(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                       int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* order);
 
 // Enqueue the standalone merge (o_acc, lse_acc) <- merge(acc, part).
 hipError_t launch_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part, int out_bf16,

@@ -77,7 +77,9 @@
 //    sum and unnormalised O stay in registers, so O is written once.
 //  * Float32 inputs use the same skeleton with v_mfma_f32_32x32x2_f32 and
 //    32-key tiles.
+#include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -138,7 +140,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int g = lane >> 5;                // half-wave
   const int li = lane & 31;               // query row within the wave
 
-  const int Lid = tile_order(blockIdx.x, p.n_wg, p.n_hgroups);
+  // (a caller's dispatch order is clamped into range: a wrong one gives wrong
+  // results, never an access outside the tensors)
+  const int Lid = p.wg_order ? min(max(p.wg_order[blockIdx.x], 0), p.n_wg - 1)
+                             : tile_order(blockIdx.x, p.n_wg, p.n_hgroups);
   const int hgrp = Lid / p.n_qtiles;
   const int qt = p.n_qtiles - 1 - (Lid % p.n_qtiles);  // late (heavier) rows first
   const int hsub = wave % p.g_wg, rb = wave / p.g_wg;
@@ -851,18 +856,68 @@ static hipError_t launch_typed(const PartialParams& p, const BlockTable& bt, boo
   return hipGetLastError();
 }
 
-static hipError_t launch_any(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
-                             bool varlen, bool multi, hipStream_t stream) {
-  // a workgroup: g_wg query heads of one KV group x r_wg blocks of 32 rows, g_wg * r_wg = kWaves
+// Workgroup geometry: g_wg query heads of one KV group x r_wg blocks of 32
+// rows (g_wg * r_wg = kWaves); returns the number of workgroups.
+static int64_t set_geometry(PartialParams& p) {
   const int G = p.hq / p.hkv;
   p.g_wg = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   p.r_wg = kWaves / p.g_wg;
   p.n_qtiles = (int32_t)((p.lq + 32 * p.r_wg - 1) / (32 * p.r_wg));
   p.n_hgroups = p.hq / p.g_wg;
-  const int64_t n_wg = (int64_t)p.n_qtiles * p.n_hgroups;
+  return (int64_t)p.n_qtiles * p.n_hgroups;
+}
+
+int64_t partial_workgroups(int64_t lq, int32_t hq, int32_t hkv) {
+  PartialParams p{};
+  p.lq = lq; p.hq = hq; p.hkv = hkv;
+  return set_geometry(p);
+}
+
+// Key tiles that the workgroup of logical tile L loads (host mirror of the
+// kernel's key range: from the first row's document start to the last row).
+static int64_t host_upper_bound(const int32_t* a, int64_t n, int32_t x) {
+  return std::upper_bound(a, a + n, x) - a;
+}
+
+void plan_varlen_order(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                       int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* order) {
+  PartialParams p{};
+  p.lq = lq; p.hq = hq; p.hkv = hkv;
+  const int64_t n = set_geometry(p);
+  const int BK = in_bf16 ? (head_dim == 64 ? Cfg<__bf16, 64, kWaves>::kBK : Cfg<__bf16, 128, kWaves>::kBK)
+                         : Cfg<float, 128, kWaves>::kBK;
+  std::vector<int64_t> work((size_t)n, 0);
+  for (int64_t L = 0; L < n; ++L) {
+    const int64_t qt = p.n_qtiles - 1 - L % p.n_qtiles;
+    const int64_t r0 = qt * 32 * p.r_wg, r1 = std::min<int64_t>(r0 + 32 * p.r_wg, lq);
+    if (lk == 0 || k_pos[0] > q_pos[r1 - 1]) continue;  // sees nothing of the block
+    const int64_t di = host_upper_bound(cu_seqlens, (int64_t)n_seqs + 1, q_pos[r0]) - 1;
+    const int32_t s_wg = cu_seqlens[di < 0 ? 0 : di];
+    const int64_t kb = std::lower_bound(k_pos, k_pos + lk, s_wg) - k_pos;
+    const int64_t ke = host_upper_bound(k_pos, lk, q_pos[r1 - 1]);
+    if (ke > kb) work[(size_t)L] = (ke + BK - 1) / BK - kb / BK;
+  }
+  // Workgroup id b runs on XCD b % 8; each XCD keeps the logical tiles the
+  // default order gives it (shared K/V in its L2), heaviest first (longest
+  // processing time first: the XCD's CUs then finish close together).
+  for (int x = 0; x < 8; ++x) {
+    std::vector<int32_t> ls;
+    for (int64_t b = x; b < n; b += 8) ls.push_back(tile_order((int)b, (int)n, p.n_hgroups));
+    std::stable_sort(ls.begin(), ls.end(), [&](int32_t a, int32_t c) {
+      return work[(size_t)a] != work[(size_t)c] ? work[(size_t)a] > work[(size_t)c] : a < c;
+    });
+    size_t i = 0;
+    for (int64_t b = x; b < n; b += 8) order[b] = ls[i++];
+  }
+}
+
+static hipError_t launch_any(PartialParams p, const BlockTable& bt, int in_bf16, int out_bf16, int head_dim,
+                             bool varlen, bool multi, hipStream_t stream) {
+  const int64_t n_wg = set_geometry(p);
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   p.n_wg = (int32_t)n_wg;
+  if (multi) p.wg_order = nullptr;
   if (in_bf16) {
     if (head_dim == 128) return out_bf16 ? launch_typed<__bf16, __bf16, 128>(p, bt, varlen, multi, stream)
                                          : launch_typed<__bf16, float, 128>(p, bt, varlen, multi, stream);

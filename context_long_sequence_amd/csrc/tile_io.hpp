@@ -53,7 +53,7 @@ struct Cfg {
 // Workgroup id -> logical tile id. Hardware dispatches consecutive workgroup
 // ids round-robin over the 8 XCDs; this gives XCD x a contiguous range of
 // logical ids, so tiles of the same head share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   int x = bid & 7, slot = bid >> 3;
   int q = n >> 3, rem = n & 7;
   return x * q + (x < rem ? x : rem) + slot;
@@ -66,7 +66,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // give one XCD all the heaviest tiles (two units of 4096 tiles: 1.75 times
 // the mean work), so the hardware's round-robin order is kept, which hands
 // every XCD every eighth tile of the heavy-first order.
-__device__ __forceinline__ int tile_order(int bid, int n, int units) {
+__host__ __device__ __forceinline__ int tile_order(int bid, int n, int units) {
   return (units & 7) == 0 ? xcd_remap(bid, n) : bid;
 }
 

@@ -336,11 +336,22 @@ def fetch_positions(mem, src, r0s, lims, wave, BK=64):
 # ---------------------------------------------------------------------------
 # partial-attention kernel (partial_fwd.hip)
 
+def fwd_workgroups(lq, hq, hkv):
+    """Workgroups of one forward launch (8 waves: query heads of one KV group x 32-row blocks)."""
+    G = hq // hkv
+    g_wg = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    r_wg = 8 // g_wg
+    return ((lq + 32 * r_wg - 1) // (32 * r_wg)) * (hq // g_wg)
+
+
 def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumulate, blocks, varlen=False,
-                   n_seqs=0, multi=False):
+                   n_seqs=0, multi=False, ordered=False):
     """One launch of the partial-attention kernel. blocks: list of
     (k tensor, v tensor, k_pos array name, lk) — one for a single-block call.
-    Tensors: 'q', 'o', 'lse', 'q_pos', 'cu'. Returns the K/V tiles loaded."""
+    Tensors: 'q', 'o', 'lse', 'q_pos', 'cu' (and 'wg_order' when `ordered`: a
+    caller's dispatch order, whose entries the kernel clamps into [0, n_wg),
+    so every logical tile replayed below covers whatever it holds). Returns
+    the K/V tiles loaded."""
     c = FwdCfg(in_bf16, D)
     G = hq // hkv
     g_wg = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
@@ -350,6 +361,8 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
     if n_wg <= 0:
         return 0
     check_remap(n_wg)
+    if ordered and not multi:
+        mem.index("wg_order", np.arange(n_wg, dtype=np.int64), "wg_order[blockIdx]")
     deep = False  # (two-ahead staging sets are no longer used)
     osz = 2 if out_bf16 else 4
     row_stride = hkv * D * c.esz

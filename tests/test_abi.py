@@ -17,7 +17,8 @@ def test_exports_every_declared_symbol(lib):
     names = cp.header_functions()
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
                           "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse", "cpattn_bwd_delta",
-                          "cpattn_partial_bwd"}
+                          "cpattn_partial_bwd", "cpattn_partial_workgroups", "cpattn_varlen_plan",
+                          "cpattn_varlen_partial_ordered"}
     for n in names:
         assert hasattr(lib, n), n
 

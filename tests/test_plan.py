@@ -1,0 +1,184 @@
+"""The dispatch order of the document calls (cpattn_varlen_plan).
+
+Host logic (CPU): the order is a permutation of the call's workgroups; each
+XCD (workgroup id b runs on XCD b % 8) keeps the set of logical tiles the
+kernel's default order gives it; within an XCD the tiles go in decreasing
+order of the key tiles their workgroup loads, ties by logical id. The work of
+a tile is recomputed here from the positions, and on a small case by brute
+force over keys. GPU: the ordered call gives bit-identical results to the
+default order (each logical tile owns its rows).
+"""
+import numpy as np
+import pytest
+
+import context_long_sequence_amd as cp
+from context_long_sequence_amd.share import block_positions
+
+
+def _geometry(lq, hq, hkv):
+    G = hq // hkv
+    g_wg = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    r_wg = 8 // g_wg
+    n_qtiles = (lq + 32 * r_wg - 1) // (32 * r_wg)
+    return n_qtiles, hq // g_wg, r_wg
+
+
+def _default_logical(n, units):
+    """Logical tile of each workgroup id in the kernel's default order."""
+    bid = np.arange(n, dtype=np.int64)
+    if units % 8 != 0:
+        return bid
+    x, slot = bid & 7, bid >> 3
+    q, rem = n >> 3, n & 7
+    return x * q + np.minimum(x, rem) + slot
+
+
+def _tile_keys(in_bf16, d):
+    return (128 if d == 64 else 64) if in_bf16 else 32
+
+
+def _work(q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16):
+    """Key tiles each logical tile's workgroup loads: keys from the first row's
+    document start to the last row's position."""
+    n_qtiles, units, r_wg = _geometry(lq, hq, hkv)
+    BK = _tile_keys(in_bf16, d)
+    L = np.arange(n_qtiles * units, dtype=np.int64)
+    qt = n_qtiles - 1 - L % n_qtiles
+    r0 = qt * 32 * r_wg
+    r1 = np.minimum(r0 + 32 * r_wg, lq)
+    first, last = q_pos[r0], q_pos[r1 - 1]
+    start = cu[np.searchsorted(cu, first, side="right") - 1]
+    kb = np.searchsorted(k_pos, start, side="left")
+    ke = np.searchsorted(k_pos, last, side="right")
+    nt = np.where(ke > kb, (ke + BK - 1) // BK - kb // BK, 0)
+    if len(k_pos) == 0:
+        return np.zeros_like(nt)
+    return np.where(k_pos[0] > last, 0, nt)
+
+
+def _check_plan(order, q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16):
+    n_qtiles, units, _ = _geometry(lq, hq, hkv)
+    n = n_qtiles * units
+    assert len(order) == n == cp.cpattn_partial_workgroups(lq, hq, hkv)
+    assert np.array_equal(np.sort(order), np.arange(n)), "not a permutation"
+    work = _work(q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16)
+    default = _default_logical(n, units)
+    for x in range(8):
+        ids = order[x::8].astype(np.int64)
+        assert np.array_equal(np.sort(ids), np.sort(default[x::8])), "XCD %d's set changed" % x
+        w = work[ids]
+        assert np.all(np.diff(w) <= 0), "XCD %d: work not non-increasing" % x
+        ties = np.diff(w) == 0
+        assert np.all(np.diff(ids)[ties] > 0), "XCD %d: ties not by logical id" % x
+    return work
+
+
+def _documents_share(S, cp_size, docs_seed, min_doc, max_doc):
+    """cu_seqlens of seeded document lengths (multiples of 2 cp_size, as the
+    per-document zig-zag split needs) that fill S."""
+    rng = np.random.default_rng(docs_seed)
+    u = 2 * cp_size
+    lens = []
+    while sum(lens) < S:
+        lens.append(u * int(rng.integers(max(1, min_doc // u), max_doc // u + 1)))
+    lens[-1] -= sum(lens) - S
+    if lens[-1] <= 0:
+        extra = lens.pop()
+        lens[-1] += extra
+    assert sum(lens) == S and all(x > 0 and x % u == 0 for x in lens)
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("S,cp_size,rank,hq,hkv,d,in_bf16", [
+    (131072, 4, 1, 32, 32, 128, True),     # the documents share: 32 heads (units split over the 8 XCDs)
+    (16384, 4, 2, 16, 2, 64, True),        # grouped KV heads, d 64 (2 units: the hardware's order)
+    (8192, 4, 0, 4, 4, 128, False),        # float32 tiles
+])
+def test_plan_keeps_xcd_sets_and_orders_by_work(S, cp_size, rank, hq, hkv, d, in_bf16):
+    cu = _documents_share(S, cp_size, 11, 256, 8192)
+    q_pos, _ = cp.cpattn_zigzag_index(S, cp_size, rank, "zigzag", cu)
+    kps = block_positions(S, cp_size, cp_size, "rank_shares", "zigzag", cu)
+    lq = len(q_pos)
+    for b, kp in enumerate(kps):
+        order = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d, "bf16" if in_bf16 else "f32")
+        work = _check_plan(order, q_pos, kp, cu, lq, hq, hkv, d, in_bf16)
+        assert work.max() > 0
+        again = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d, "bf16" if in_bf16 else "f32")
+        assert np.array_equal(order, again), "the plan must be deterministic"
+
+
+def test_work_estimate_brute_force():
+    """On a small share, the work of each tile equals the key tiles spanned
+    from the first key at or after the first row's document start to the last
+    key at or before the last row, found by scanning every key."""
+    S, cps = 4096, 4
+    cu = _documents_share(S, cps, 5, 64, 700)
+    q_pos, _ = cp.cpattn_zigzag_index(S, cps, 3, "zigzag", cu)
+    kps = block_positions(S, cps, cps, "rank_shares", "zigzag", cu)
+    hq = hkv = 8
+    d = 128
+    n_qtiles, units, r_wg = _geometry(len(q_pos), hq, hkv)
+    BK = _tile_keys(True, d)
+    for kp in kps:
+        order = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d)
+        work = _check_plan(order, q_pos, kp, cu, len(q_pos), hq, hkv, d, True)
+        for L in range(n_qtiles * units):
+            qt = n_qtiles - 1 - L % n_qtiles
+            r0 = qt * 32 * r_wg
+            r1 = min(r0 + 32 * r_wg, len(q_pos))
+            start = max(c for c in cu[:-1] if c <= q_pos[r0])
+            if kp[0] > q_pos[r1 - 1]:
+                want = 0
+            else:
+                kb = next((j for j in range(len(kp)) if kp[j] >= start), len(kp))
+                ke = max((j + 1 for j in range(len(kp)) if kp[j] <= q_pos[r1 - 1]), default=0)
+                want = -(-ke // BK) - kb // BK if ke > kb else 0
+            assert work[L] == want, (L, work[L], want)
+
+
+def test_plan_errors():
+    q_pos = np.arange(256, dtype=np.int32)
+    k_pos = np.arange(256, dtype=np.int32)
+    cu = np.array([0, 100, 256], np.int32)
+    lib = cp.load_library()
+    n = cp.cpattn_partial_workgroups(256, 4, 4)
+    out = np.zeros(n + 1, np.int32)
+    st = lib.cpattn_varlen_plan(q_pos.ctypes.data, 256, k_pos.ctypes.data, 256, cu.ctypes.data, 2, 4, 4, 128, 0,
+                                out.ctypes.data, n + 1)
+    assert st == 2  # CPATTN_ERR_SHAPE: n_order is not the workgroup count
+    bad = q_pos[::-1].copy()
+    with pytest.raises(cp.CpattnError) as e:
+        cp.cpattn_varlen_plan(bad, k_pos, cu, 4, 4, 128)
+    assert e.value.status == 4  # CPATTN_ERR_UNSORTED
+    with pytest.raises(cp.CpattnError) as e:
+        cp.cpattn_varlen_plan(q_pos, k_pos, cu, 4, 4, 96)
+    assert e.value.status == 2
+    assert cp.cpattn_partial_workgroups(-1, 4, 4) == -1
+    assert cp.cpattn_partial_workgroups(256, 6, 4) == -1
+    assert cp.cpattn_partial_workgroups(0, 4, 4) == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["docs8k_zigzag_cp4_h4_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
+def test_ordered_calls_bit_identical(name):
+    """The share's planned dispatch orders, a random permutation and the
+    default order give bit-identical O and LSE (accumulate mode, every block)."""
+    import torch
+    from test_gpu_parity import _reduced, say
+    from context_long_sequence_amd.share import share_from_workload
+    wl = _reduced()[name]
+    say("%s: planned / random / default dispatch order" % name)
+    planned = share_from_workload(wl)
+    assert planned.wg_orders is not None
+    o1, l1 = [t.clone() for t in planned.step(wl.arrival())]
+    n = planned.wg_orders[0].numel()
+    rng = np.random.default_rng(3)
+    planned.wg_orders = [torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda() for _ in planned.wg_orders]
+    o2, l2 = [t.clone() for t in planned.step(wl.arrival())]
+    plain = share_from_workload(wl, plan=False)
+    assert plain.wg_orders is None
+    o3, l3 = plain.step(wl.arrival())
+    torch.cuda.synchronize()
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
+        assert torch.equal(l1, l)
