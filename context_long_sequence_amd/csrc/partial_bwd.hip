@@ -596,6 +596,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
     const char CPATTN_LDS* vl = st ? (const char CPATTN_LDS*)v_s1 : (const char CPATTN_LDS*)v_s0;
     const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
 
+    // (the products run at raised priority: the other workgroup's wave on the
+    // SIMD then issues its vector work around them rather than in their way)
+    __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query
     // row), alternating so that neither chain waits on its own previous MFMA;
     // operands read RING ahead
@@ -619,6 +622,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile.
     // Without documents, a tile of 32 keys inside the block that are all at
     // or before the wave's first row is seen in full by every row of the wave
@@ -654,6 +658,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
     if (full) dsoft(std::false_type{});
     else dsoft(std::true_type{});
 
+    __builtin_amdgcn_s_setprio(1);
     // dQ^T += K^T dS^T (K^T read transposed, RING ahead)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     {
@@ -674,6 +679,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < nt) commit(st ^ 1);
     // Nothing is in flight here (the commit waited for its loads). Saying so
     // keeps the compiler's wait analysis exact across the conditional commit:
