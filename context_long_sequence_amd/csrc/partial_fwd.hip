@@ -233,7 +233,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // workgroup's first row and of the wave's last row, and this lane's own. The
   // three document indices are searched together; when the wave's first and
   // last rows share a document (nearly always) every lane's start is that
-  // document's, and only a wave across a document boundary searches per lane.
+  // document's; when they lie in adjacent documents a lane's start is the
+  // last row's document start if its position has reached it, else the first
+  // row's (rows ascend); only a wave across three or more documents searches
+  // per lane.
   int32_t s_wg = 0, s_wave = 0, my_start = 0;
   if constexpr (VARLEN) {
     if (p.causal) {
@@ -247,7 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       wave_upper_bounds<3>(cus, ns, xs, d);
       s_wg = p.cu_seqlens[d[0] > 0 ? d[0] - 1 : 0];
       s_wave = p.cu_seqlens[d[2] > 0 ? d[2] - 1 : 0];
-      my_start = d[1] == d[2] ? s_wave : doc_start(p.cu_seqlens, p.n_seqs, my_qpos);
+      const int32_t s_first = p.cu_seqlens[d[1] > 0 ? d[1] - 1 : 0];
+      my_start = d[1] == d[2]       ? s_wave
+                 : d[2] == d[1] + 1 ? (my_qpos >= s_wave ? s_wave : s_first)
+                                    : doc_start(p.cu_seqlens, p.n_seqs, my_qpos);
     }
   }
 

@@ -396,10 +396,10 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
         d0 = sr.wave_upper_bound("cu", n_seqs + 1, qp[wg_r0])
         d1 = sr.wave_upper_bound("cu", n_seqs + 1, qp[i_first])
         d2 = sr.wave_upper_bound("cu", n_seqs + 1, qp[i_last])
-        j0, j2 = np.where(d0 > 0, d0 - 1, 0), np.where(d2 > 0, d2 - 1, 0)
-        mem.index("cu", np.stack([j0, j2]))
+        j0, j1, j2 = np.where(d0 > 0, d0 - 1, 0), np.where(d1 > 0, d1 - 1, 0), np.where(d2 > 0, d2 - 1, 0)
+        mem.index("cu", np.stack([j0, j1, j2]))
         s_wg, s_wave = sr.arrays["cu"][j0].astype(np.int64), sr.arrays["cu"][j2].astype(np.int64)
-        across = d1 != d2  # a wave across a document boundary: per-lane starts
+        across = d2 > d1 + 1  # a wave across three or more documents: per-lane starts
         if across.any():
             sr.doc_start("cu", n_seqs, qp[qi[across]])
 

@@ -120,13 +120,18 @@ def _reduced():
         zz1m.scaled(name="zigzag16k_cp8_h8kv2_d128", S=16384, hq=8, hkv=2),
         # documents at d 64 with grouped KV heads
         docs.scaled(name="docs8k_zigzag_cp4_h4kv2_d64", S=8192, hq=4, hkv=2, d=64, sigma=1.0, docs=(256, 2048)),
+        # short documents: 32-row waves across two documents (64..512 tokens,
+        # chunks of 8..64 rows) and across many (8..96 tokens, 1..12 rows)
+        docs.scaled(name="docs4k_zigzag_cp4_h2_d128_short", S=4096, hq=2, hkv=2, docs=(64, 512)),
+        docs.scaled(name="docs4k_zigzag_cp4_h2kv1_d64_tiny", S=4096, hq=2, hkv=1, d=64, docs=(8, 96)),
     ]
     return {w.name: w for w in wls}
 
 
 @pytest.mark.parametrize("name", ["zigzag1k_cp4_h1_d64_f32", "zigzag4k_cp8_h4_d128", "contig2k_h16kv2_d64",
                                   "docs8k_zigzag_cp4_h4_d128", "zigzag16k_cp8_h8kv2_d128",
-                                  "docs8k_zigzag_cp4_h4kv2_d64"])
+                                  "docs8k_zigzag_cp4_h4kv2_d64", "docs4k_zigzag_cp4_h2_d128_short",
+                                  "docs4k_zigzag_cp4_h2kv1_d64_tiny"])
 @pytest.mark.parametrize("mode", ["accumulate", "merge"])
 def test_reduced_all_rows(torch_cuda, orc, name, mode):
     from context_long_sequence_amd.share import share_from_workload
