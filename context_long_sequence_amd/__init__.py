@@ -73,8 +73,8 @@ def load_library(path=LIB_PATH):
     lib.cpattn_partial_workgroups.argtypes = [i64, i32, i32]
     lib.cpattn_varlen_plan.restype = ctypes.c_int
     lib.cpattn_varlen_plan.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, i32, ctypes.c_int, vp, i64]
-    lib.cpattn_varlen_partial_ordered.restype = ctypes.c_int
-    lib.cpattn_varlen_partial_ordered.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32,
+    lib.cpattn_varlen_partial_planned.restype = ctypes.c_int
+    lib.cpattn_varlen_partial_planned.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32,
                                                   f32, vp, ctypes.c_int, vp, i32, vp, i64, vp]
     lib.cpattn_partial_multi.restype = ctypes.c_int
     lib.cpattn_partial_multi.argtypes = [vp, vp, vp, ctypes.c_int, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32,
@@ -185,10 +185,10 @@ def cpattn_partial(q, k, v, q_pos, k_pos, o, lse, causal=True, softmax_scale=0.0
 
 
 def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_scale=0.0, accumulate=False,
-                          stream=None, wg_order=None):
+                          stream=None, plan=None):
     """As cpattn_partial, causal within documents given by device cu_seqlens.
-    wg_order (optional int32 device tensor, from cpattn_varlen_plan): the
-    dispatch order (cpattn_varlen_partial_ordered)."""
+    plan (optional int32 device tensor, from cpattn_varlen_plan for these
+    positions): the call runs planned (cpattn_varlen_partial_planned)."""
     import torch
     lib = load_library()
     lq, lk, hq, hkv, d = _shapes(q, k, o, lse)
@@ -202,13 +202,12 @@ def cpattn_varlen_partial(q, k, v, q_pos, k_pos, cu_seqlens, o, lse, softmax_sca
             _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
             _dev(cu_seqlens, "cu_seqlens", torch.int32), cu_seqlens.numel() - 1, float(softmax_scale), _dev(o, "o"),
             _dtype_code(o), _dev(lse, "lse", torch.float32), int(bool(accumulate))]
-    if wg_order is None:
+    if plan is None:
         st = lib.cpattn_varlen_partial(*args, _stream(stream))
     else:
-        if wg_order.dim() != 1:
-            raise CpattnError(2, "wg_order must be 1-D")
-        st = lib.cpattn_varlen_partial_ordered(*args, _dev(wg_order, "wg_order", torch.int32), wg_order.numel(),
-                                               _stream(stream))
+        if plan.dim() != 1:
+            raise CpattnError(2, "plan must be 1-D")
+        st = lib.cpattn_varlen_partial_planned(*args, _dev(plan, "plan", torch.int32), plan.numel(), _stream(stream))
     _check(lib, st)
 
 
@@ -217,9 +216,13 @@ def cpattn_partial_workgroups(lq, hq, hkv):
     return int(load_library().cpattn_partial_workgroups(int(lq), int(hq), int(hkv)))
 
 
+VARLEN_PLAN_RECORD = 48  # CPATTN_VARLEN_PLAN_RECORD: int32 per workgroup in a plan
+
+
 def cpattn_varlen_plan(q_pos, k_pos, cu_seqlens, hq, hkv, head_dim, in_dtype="bf16"):
-    """Dispatch order for cpattn_varlen_partial(..., wg_order=) from HOST
-    positions and document offsets (numpy int32): an int32 numpy array."""
+    """Plan of one document call (cpattn_varlen_partial(..., plan=)) from HOST
+    positions and document offsets (numpy int32): an int32 numpy array of
+    VARLEN_PLAN_RECORD entries per workgroup."""
     lib = load_library()
     qp = np.ascontiguousarray(q_pos, np.int32)
     kp = np.ascontiguousarray(k_pos, np.int32)
@@ -227,13 +230,14 @@ def cpattn_varlen_plan(q_pos, k_pos, cu_seqlens, hq, hkv, head_dim, in_dtype="bf
     n = cpattn_partial_workgroups(len(qp), hq, hkv)
     if n < 0:
         raise CpattnError(2, "invalid sizes lq=%d hq=%d hkv=%d" % (len(qp), hq, hkv))
-    order = np.zeros(max(n, 1), np.int32)
+    n *= VARLEN_PLAN_RECORD
+    plan = np.zeros(max(n, 1), np.int32)
     code = in_dtype if isinstance(in_dtype, int) else (CPATTN_BF16 if in_dtype == "bf16" else CPATTN_F32)
     st = lib.cpattn_varlen_plan(qp.ctypes.data, len(qp), kp.ctypes.data if len(kp) else None, len(kp),
                                 cu.ctypes.data, len(cu) - 1, int(hq), int(hkv), int(head_dim), code,
-                                order.ctypes.data, n)
+                                plan.ctypes.data, n)
     _check(lib, st)
-    return order[:n]
+    return plan[:n]
 
 
 def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,

@@ -15,6 +15,8 @@
 #include "kernels.hpp"
 #include "kernels_bwd.hpp"
 
+static_assert(CPATTN_VARLEN_PLAN_RECORD == cpattn::kPlanRec, "plan record size");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -62,21 +64,26 @@ cpattn_status check_sorted_device(const int32_t* dptr, int64_t n, const char* na
   return CPATTN_OK;
 }
 
-// Optional O(n) check that a device dispatch order is a permutation of [0, n)
-// (synchronises `stream`).
-cpattn_status check_permutation_device(const int32_t* dptr, int64_t n, hipStream_t stream) {
-  std::vector<int32_t> h((size_t)n);
-  hipError_t e = hipMemcpyAsync(h.data(), dptr, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+// Optional check that a device plan is the one cpattn_varlen_plan makes for
+// these positions (synchronises `stream`; copies the positions and the plan).
+cpattn_status check_plan_device(const int32_t* dplan, const int32_t* q_pos, int64_t lq, const int32_t* k_pos,
+                                int64_t lk, const int32_t* cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                int in_bf16, int32_t head_dim, hipStream_t stream) {
+  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv) * cpattn::kPlanRec;
+  std::vector<int32_t> plan((size_t)n), qp((size_t)lq), kp((size_t)lk), cu((size_t)n_seqs + 1), want((size_t)n);
+  hipError_t e = hipMemcpyAsync(plan.data(), dplan, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(qp.data(), q_pos, sizeof(int32_t) * (size_t)lq, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && lk > 0)
+    e = hipMemcpyAsync(kp.data(), k_pos, sizeof(int32_t) * (size_t)lk, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * ((size_t)n_seqs + 1), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "reading wg_order for validation: %s", hipGetErrorString(e));
-  std::vector<char> seen((size_t)n, 0);
-  for (int64_t i = 0; i < n; ++i) {
-    const int32_t x = h[(size_t)i];
-    if (x < 0 || x >= n || seen[(size_t)x])
-      return fail(CPATTN_ERR_RANGE, "wg_order is not a permutation of [0, %lld): entry %lld is %d", (long long)n,
-                  (long long)i, x);
-    seen[(size_t)x] = 1;
-  }
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "reading the plan for validation: %s", hipGetErrorString(e));
+  cpattn::plan_varlen(qp.data(), lq, kp.data(), lk, cu.data(), n_seqs, hq, hkv, in_bf16, head_dim, want.data());
+  for (int64_t i = 0; i < n; ++i)
+    if (plan[(size_t)i] != want[(size_t)i])
+      return fail(CPATTN_ERR_RANGE, "the plan differs from cpattn_varlen_plan's at entry %lld (%d, expected %d)",
+                  (long long)i, plan[(size_t)i], want[(size_t)i]);
   return CPATTN_OK;
 }
 
@@ -124,13 +131,15 @@ cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpatt
                               int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
                               const int32_t* k_pos, const int32_t* cu_seqlens, int32_t n_seqs, int32_t causal,
                               float softmax_scale, void* o, cpattn_dtype o_dtype, float* lse, int32_t accumulate,
-                              void* stream, const int32_t* wg_order = nullptr) {
+                              void* stream, const int32_t* plan = nullptr) {
   hipStream_t s = (hipStream_t)stream;
   if (validate_env() && causal) {
     cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
     if (st == CPATTN_OK) st = check_sorted_device(k_pos, lk, "k_pos", s);
     if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
-    if (st == CPATTN_OK && wg_order) st = check_permutation_device(wg_order, cpattn::partial_workgroups(lq, hq, hkv), s);
+    if (st == CPATTN_OK && plan)
+      st = check_plan_device(plan, q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, hkv, in_dtype == CPATTN_BF16,
+                             head_dim, s);
     if (st != CPATTN_OK) return st;
   }
   if (lq == 0) return ok();
@@ -141,7 +150,7 @@ cpattn_status enqueue_partial(const void* q, const void* k, const void* v, cpatt
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal; p.accumulate = accumulate;
-  p.wg_order = wg_order;
+  p.wg_plan = plan;
   hipError_t e = cpattn::launch_partial(p, in_dtype == CPATTN_BF16, o_dtype == CPATTN_BF16, head_dim,
                                         cu_seqlens != nullptr, s);
   if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -278,7 +287,7 @@ int64_t cpattn_partial_workgroups(int64_t lq, int32_t hq, int32_t hkv) {
 
 cpattn_status cpattn_varlen_plan(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk,
                                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
-                                 int32_t head_dim, cpattn_dtype in_dtype, int32_t* order, int64_t n_order) {
+                                 int32_t head_dim, cpattn_dtype in_dtype, int32_t* plan, int64_t plan_len) {
   if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
   if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
@@ -286,12 +295,12 @@ cpattn_status cpattn_varlen_plan(const int32_t* q_pos, int64_t lq, const int32_t
   if (head_dim != 64 && head_dim != 128) return fail(CPATTN_ERR_SHAPE, "head_dim must be 64 or 128, got %d", head_dim);
   if (in_dtype != CPATTN_BF16 && in_dtype != CPATTN_F32) return fail(CPATTN_ERR_DTYPE, "in_dtype must be bf16 or float32");
   if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
-  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv);
-  if (n_order != n) return fail(CPATTN_ERR_SHAPE, "n_order must be %lld (the call's workgroups), got %lld",
-                                (long long)n, (long long)n_order);
+  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv) * CPATTN_VARLEN_PLAN_RECORD;
+  if (plan_len != n) return fail(CPATTN_ERR_SHAPE, "plan_len must be %lld (the call's workgroups x %d), got %lld",
+                                 (long long)n, CPATTN_VARLEN_PLAN_RECORD, (long long)plan_len);
   if (n == 0) return ok();
-  if (!q_pos || !cu_seqlens || !order || (lk > 0 && !k_pos))
-    return fail(CPATTN_ERR_NULL, "q_pos, k_pos, cu_seqlens and order must be non-NULL");
+  if (!q_pos || !cu_seqlens || !plan || (lk > 0 && !k_pos))
+    return fail(CPATTN_ERR_NULL, "q_pos, k_pos, cu_seqlens and plan must be non-NULL");
   for (int64_t i = 1; i < lq; ++i)
     if (q_pos[i] < q_pos[i - 1]) return fail(CPATTN_ERR_UNSORTED, "q_pos is not ascending at index %lld", (long long)i);
   for (int64_t i = 1; i < lk; ++i)
@@ -299,17 +308,16 @@ cpattn_status cpattn_varlen_plan(const int32_t* q_pos, int64_t lq, const int32_t
   for (int32_t i = 1; i <= n_seqs; ++i)
     if (cu_seqlens[i] < cu_seqlens[i - 1])
       return fail(CPATTN_ERR_UNSORTED, "cu_seqlens is not ascending at index %d", i);
-  cpattn::plan_varlen_order(q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, hkv, in_dtype == CPATTN_BF16, head_dim,
-                            order);
+  cpattn::plan_varlen(q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, hkv, in_dtype == CPATTN_BF16, head_dim, plan);
   return ok();
 }
 
-cpattn_status cpattn_varlen_partial_ordered(const void* q, const void* k, const void* v, cpattn_dtype in_dtype,
+cpattn_status cpattn_varlen_partial_planned(const void* q, const void* k, const void* v, cpattn_dtype in_dtype,
                                             int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
                                             const int32_t* q_pos, const int32_t* k_pos, const int32_t* cu_seqlens,
                                             int32_t n_seqs, float softmax_scale, void* o, cpattn_dtype o_dtype,
-                                            float* lse, int32_t accumulate, const int32_t* wg_order,
-                                            int64_t n_order, void* stream) {
+                                            float* lse, int32_t accumulate, const int32_t* plan, int64_t plan_len,
+                                            void* stream) {
   cpattn_status st = check_partial_args(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, 1, o, o_dtype,
                                         lse, accumulate);
   if (st != CPATTN_OK) return st;
@@ -317,13 +325,13 @@ cpattn_status cpattn_varlen_partial_ordered(const void* q, const void* k, const 
   if (!aligned(cu_seqlens, 4)) return fail(CPATTN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
   if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
   if (!std::isfinite(softmax_scale)) return fail(CPATTN_ERR_RANGE, "softmax_scale must be finite");
-  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv);
-  if (n_order != n) return fail(CPATTN_ERR_SHAPE, "n_order must be %lld (the call's workgroups), got %lld",
-                                (long long)n, (long long)n_order);
-  if (n > 0 && !wg_order) return fail(CPATTN_ERR_NULL, "wg_order must be non-NULL");
-  if (!aligned(wg_order, 4)) return fail(CPATTN_ERR_ALIGN, "wg_order must be 4-byte aligned");
+  const int64_t n = cpattn::partial_workgroups(lq, hq, hkv) * CPATTN_VARLEN_PLAN_RECORD;
+  if (plan_len != n) return fail(CPATTN_ERR_SHAPE, "plan_len must be %lld (the call's workgroups x %d), got %lld",
+                                 (long long)n, CPATTN_VARLEN_PLAN_RECORD, (long long)plan_len);
+  if (n > 0 && !plan) return fail(CPATTN_ERR_NULL, "plan must be non-NULL");
+  if (!aligned(plan, 4)) return fail(CPATTN_ERR_ALIGN, "plan must be 4-byte aligned");
   return enqueue_partial(q, k, v, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, cu_seqlens, n_seqs, 1,
-                         softmax_scale, o, o_dtype, lse, accumulate, stream, n > 0 ? wg_order : nullptr);
+                         softmax_scale, o, o_dtype, lse, accumulate, stream, n > 0 ? plan : nullptr);
 }
 
 cpattn_status cpattn_partial_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,

@@ -23,8 +23,16 @@ struct PartialParams {
   int32_t n_qtiles, n_hgroups, n_wg;
   float scale_log2;           // softmax scale * log2(e)
   int32_t causal, accumulate;
-  const int32_t* wg_order;    // optional dispatch order: logical tile of each workgroup id (else tile_order)
+  const int32_t* wg_plan;     // optional plan of a document call: kPlanRec int32 per workgroup id (see below)
 };
+
+// A document call's plan, one record per workgroup id (made on the host by
+// plan_varlen): the logical tile it computes, its key range, and per wave the
+// document starts of its first and last rows, its fully visible key range and
+// whether its lanes must search their own document starts.
+constexpr int kPlanRec = 48;
+constexpr int kPlanTile = 0, kPlanKb = 1, kPlanKe = 2;
+constexpr int kPlanSLast = 4, kPlanSFirst = 12, kPlanFLo = 20, kPlanFHi = 28, kPlanFlags = 36;
 
 // The KV blocks of a multi-block call (passed by value as a kernel argument).
 constexpr int kMaxBlocks = 32;
@@ -46,11 +54,12 @@ hipError_t launch_partial_multi(PartialParams p, const BlockTable& bt, int in_bf
 // Workgroups of a single-block call (the length of a dispatch order).
 int64_t partial_workgroups(int64_t lq, int32_t hq, int32_t hkv);
 
-// Host: a dispatch order for a single-block call with documents (all
-// arguments in host memory, already validated): within each XCD's set of
-// logical tiles, the tiles that load the most key tiles go first.
-void plan_varlen_order(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
-                       int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* order);
+// Host: the plan of a single-block call with documents (all arguments in
+// host memory, already validated), kPlanRec int32 per workgroup: the dispatch
+// order (within each XCD's set of logical tiles, the tiles that load the most
+// key tiles first) and every range the kernel would otherwise search for.
+void plan_varlen(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                 int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* plan);
 
 // Enqueue the standalone merge (o_acc, lse_acc) <- merge(acc, part).
 hipError_t launch_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part, int out_bf16,

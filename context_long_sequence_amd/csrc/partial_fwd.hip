@@ -140,10 +140,13 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int g = lane >> 5;                // half-wave
   const int li = lane & 31;               // query row within the wave
 
-  // (a caller's dispatch order is clamped into range: a wrong one gives wrong
-  // results, never an access outside the tensors)
-  const int Lid = p.wg_order ? min(max(p.wg_order[blockIdx.x], 0), p.n_wg - 1)
-                             : tile_order(blockIdx.x, p.n_wg, p.n_hgroups);
+  // A planned document call takes its logical tile, key ranges and document
+  // starts from its record instead of searching for them (every value that
+  // addresses memory is clamped into range: a wrong plan gives wrong
+  // results, never an access outside the tensors).
+  const int32_t* rec = nullptr;
+  if constexpr (VARLEN && !MULTI) rec = p.wg_plan ? p.wg_plan + (int64_t)blockIdx.x * kPlanRec : nullptr;
+  const int Lid = rec ? min(max(rec[kPlanTile], 0), p.n_wg - 1) : tile_order(blockIdx.x, p.n_wg, p.n_hgroups);
   const int hgrp = Lid / p.n_qtiles;
   const int qt = p.n_qtiles - 1 - (Lid % p.n_qtiles);  // late (heavier) rows first
   const int hsub = wave % p.g_wg, rb = wave / p.g_wg;
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   const int32_t my_qpos = p.causal ? p.q_pos[qi] : 0;
   // A single-block call's first and last key, read with the first loads (the
   // emptiness test and the search shortcuts below use them).
-  const int32_t k_first0 = (!MULTI && p.causal && p.lk > 0) ? p.k_pos[0] : 0;
-  const int32_t k_last0 = (!MULTI && p.causal && p.lk > 0) ? p.k_pos[p.lk - 1] : 0;
+  const int32_t k_first0 = (!MULTI && p.causal && p.lk > 0 && !rec) ? p.k_pos[0] : 0;
+  const int32_t k_last0 = (!MULTI && p.causal && p.lk > 0 && !rec) ? p.k_pos[p.lk - 1] : 0;
   // Documents (the same for every block): the starts of the documents of the
   // workgroup's first row and of the wave's last row, and this lane's own. The
   // three document indices are searched together; when the wave's first and
@@ -239,7 +242,12 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
   // per lane.
   int32_t s_wg = 0, s_wave = 0, my_start = 0;
   if constexpr (VARLEN) {
-    if (p.causal) {
+    if (rec) {
+      s_wave = rec[kPlanSLast + wave];
+      const int32_t s_first = rec[kPlanSFirst + wave];
+      my_start = (rec[kPlanFlags + wave] & 1) ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos)
+                                              : (my_qpos >= s_wave ? s_wave : s_first);
+    } else if (p.causal) {
       const int32_t wq_lo = p.q_pos[wg_r0];
       const int32_t q_first = wave_active ? p.q_pos[r0] : p.q_pos[wg_r1 - 1];
       const int32_t q_last = wave_active ? p.q_pos[r1 - 1] : p.q_pos[wg_r1 - 1];
@@ -664,7 +672,10 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     // spares the searches below when the rows see the whole block).
     const int32_t k_first = MULTI ? ((p.causal && lk > 0) ? kpos[0] : 0) : k_first0;
     const int32_t k_last = MULTI ? ((p.causal && lk > 0) ? kpos[lk - 1] : 0) : k_last0;
-    const bool none = p.causal && (lk == 0 || k_first > p.q_pos[wg_r1 - 1]);
+    // (planned: the record's key range, empty when the rows see nothing)
+    const int p_kb = rec ? min(max(rec[kPlanKb], 0), lk) : 0;
+    const int p_ke = rec ? min(max(rec[kPlanKe], 0), lk) : 0;
+    const bool none = rec ? !(p_ke > p_kb) : p.causal && (lk == 0 || k_first > p.q_pos[wg_r1 - 1]);
     if (none || lk <= 0) {
       if (!MULTI && p.accumulate) return;
       continue;
@@ -673,8 +684,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     // then start at key 0) are requested before the key-range searches,
     // which run under their latency.
     load_q();
-    const bool early = !VARLEN;
-    if (early) load_first(0, (lk + BK - 1) / BK);  // (tiles past the workgroup's range go unread)
+    const bool early = !VARLEN || rec;
+    // (tiles past the workgroup's range go unread)
+    if (early) load_first(p_kb / BK, rec ? (p_ke + BK - 1) / BK - p_kb / BK : (lk + BK - 1) / BK);
 
     // ---- key range of the workgroup, and the per-wave fully visible range ----
     // (wave-cooperative searches: the positions are ascending, and a lower
@@ -686,7 +698,12 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
     int kb = 0, ke = lk;
     f_lo = 0;
     f_hi = lk;
-    if (p.causal) {
+    if (rec) {
+      kb = p_kb;
+      ke = p_ke;
+      f_lo = min(max(rec[kPlanFLo + wave], 0), lk);
+      f_hi = min(max(rec[kPlanFHi + wave], 0), lk);
+    } else if (p.causal) {
       // (an inactive wave, past the last row, searches with its workgroup's last row)
       const int32_t wq_hi = p.q_pos[wg_r1 - 1];
       const int32_t q_lo = wave_active ? p.q_pos[r0] : wq_hi;
@@ -879,28 +896,56 @@ int64_t partial_workgroups(int64_t lq, int32_t hq, int32_t hkv) {
   return set_geometry(p);
 }
 
-// Key tiles that the workgroup of logical tile L loads (host mirror of the
-// kernel's key range: from the first row's document start to the last row).
+// Host mirrors of the kernel's searches over ascending int32 arrays.
 static int64_t host_upper_bound(const int32_t* a, int64_t n, int32_t x) {
   return std::upper_bound(a, a + n, x) - a;
 }
+static int64_t host_lower_bound(const int32_t* a, int64_t n, int32_t x) {
+  return std::lower_bound(a, a + n, x) - a;
+}
 
-void plan_varlen_order(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
-                       int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* order) {
+void plan_varlen(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                 int32_t n_seqs, int32_t hq, int32_t hkv, int in_bf16, int head_dim, int32_t* plan) {
   PartialParams p{};
   p.lq = lq; p.hq = hq; p.hkv = hkv;
   const int64_t n = set_geometry(p);
   const int BK = in_bf16 ? (head_dim == 64 ? Cfg<__bf16, 64, kWaves>::kBK : Cfg<__bf16, 128, kWaves>::kBK)
                          : Cfg<float, 128, kWaves>::kBK;
+  // document index (as the kernel's search: offsets <= x) and start of a position
+  auto doc_idx = [&](int32_t x) { return host_upper_bound(cu_seqlens, (int64_t)n_seqs + 1, x); };
+  auto doc_at = [&](int64_t d) { return cu_seqlens[d > 0 ? d - 1 : 0]; };
+  // records by logical tile, then placed at their workgroup ids
+  std::vector<int32_t> recs((size_t)n * kPlanRec, 0);
   std::vector<int64_t> work((size_t)n, 0);
+  const int32_t k_first = lk > 0 ? k_pos[0] : 0, k_last = lk > 0 ? k_pos[lk - 1] : 0;
   for (int64_t L = 0; L < n; ++L) {
+    int32_t* r = &recs[(size_t)L * kPlanRec];
+    r[kPlanTile] = (int32_t)L;
     const int64_t qt = p.n_qtiles - 1 - L % p.n_qtiles;
-    const int64_t r0 = qt * 32 * p.r_wg, r1 = std::min<int64_t>(r0 + 32 * p.r_wg, lq);
-    if (lk == 0 || k_pos[0] > q_pos[r1 - 1]) continue;  // sees nothing of the block
-    const int64_t di = host_upper_bound(cu_seqlens, (int64_t)n_seqs + 1, q_pos[r0]) - 1;
-    const int32_t s_wg = cu_seqlens[di < 0 ? 0 : di];
-    const int64_t kb = std::lower_bound(k_pos, k_pos + lk, s_wg) - k_pos;
-    const int64_t ke = host_upper_bound(k_pos, lk, q_pos[r1 - 1]);
+    const int64_t wg_r0 = qt * 32 * p.r_wg, wg_r1 = std::min<int64_t>(wg_r0 + 32 * p.r_wg, lq);
+    const int32_t wq_hi = q_pos[wg_r1 - 1];
+    for (int w = 0; w < kWaves; ++w) {
+      // wave w's rows (the kernel's rb = w / g_wg); an inactive wave uses the
+      // workgroup's last row
+      const int64_t r0 = wg_r0 + 32 * (w / p.g_wg), r1 = std::min<int64_t>(r0 + 32, lq);
+      const bool active = r0 < lq;
+      const int32_t q_first = active ? q_pos[r0] : wq_hi, q_last = active ? q_pos[r1 - 1] : wq_hi;
+      const int64_t d1 = doc_idx(q_first), d2 = doc_idx(q_last);
+      const int32_t s_first = doc_at(d1), s_last = doc_at(d2);
+      r[kPlanSFirst + w] = s_first;
+      r[kPlanSLast + w] = s_last;
+      r[kPlanFlags + w] = d2 > d1 + 1 ? 1 : 0;  // three or more documents: per-lane starts
+      // fully visible keys: from the last row's document start to the first row
+      r[kPlanFLo + w] = (int32_t)(k_first >= s_last ? 0 : host_lower_bound(k_pos, lk, s_last));
+      r[kPlanFHi + w] = (int32_t)(k_last <= q_first ? lk : host_upper_bound(k_pos, lk, q_first));
+    }
+    // the workgroup's keys: from its first row's document start to its last row
+    if (lk == 0 || k_first > wq_hi) continue;  // sees nothing of the block (empty range)
+    const int32_t s_wg = doc_at(doc_idx(q_pos[wg_r0]));
+    const int64_t kb = k_first >= s_wg ? 0 : host_lower_bound(k_pos, lk, s_wg);
+    const int64_t ke = k_last <= wq_hi ? lk : host_upper_bound(k_pos, lk, wq_hi);
+    r[kPlanKb] = (int32_t)kb;
+    r[kPlanKe] = (int32_t)ke;
     if (ke > kb) work[(size_t)L] = (ke + BK - 1) / BK - kb / BK;
   }
   // Workgroup id b runs on XCD b % 8; each XCD keeps the logical tiles the
@@ -913,7 +958,8 @@ void plan_varlen_order(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, i
       return work[(size_t)a] != work[(size_t)c] ? work[(size_t)a] > work[(size_t)c] : a < c;
     });
     size_t i = 0;
-    for (int64_t b = x; b < n; b += 8) order[b] = ls[i++];
+    for (int64_t b = x; b < n; b += 8)
+      std::copy_n(&recs[(size_t)ls[i++] * kPlanRec], kPlanRec, plan + b * kPlanRec);
   }
 }
 
@@ -923,7 +969,7 @@ static hipError_t launch_any(PartialParams p, const BlockTable& bt, int in_bf16,
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   p.n_wg = (int32_t)n_wg;
-  if (multi) p.wg_order = nullptr;
+  if (multi || !varlen) p.wg_plan = nullptr;
   if (in_bf16) {
     if (head_dim == 128) return out_bf16 ? launch_typed<__bf16, __bf16, 128>(p, bt, varlen, multi, stream)
                                          : launch_typed<__bf16, float, 128>(p, bt, varlen, multi, stream);

@@ -54,27 +54,27 @@ class RankShare:
         self.lse = torch.empty((hq, lq), dtype=torch.float32, device=q.device)
         self._o_part = None
         self._lse_part = None
-        self.wg_orders = None   # per-block dispatch orders of the document calls (plan_orders)
+        self.plans = None   # per-block plans of the document calls (plan_blocks)
 
     @property
     def n_blocks(self):
         return len(self.k_blocks)
 
-    def plan_orders(self, q_pos_host, k_pos_host, cu_host):
-        """Dispatch orders for the document calls (cpattn_varlen_plan, from the
-        host copies of the positions), one per block; used by call_block."""
+    def plan_blocks(self, q_pos_host, k_pos_host, cu_host):
+        """Plans of the document calls (cpattn_varlen_plan, from the host copies
+        of the positions), one per block, on the device; used by call_block."""
         import torch
         lq, hq, d = self.q.shape
         hkv = self.k_blocks[0].shape[1]
         dt = "bf16" if self.q.dtype == torch.bfloat16 else "f32"
-        self.wg_orders = [torch.from_numpy(cpattn_varlen_plan(q_pos_host, kp, cu_host, hq, hkv, d, dt)).to(self.q.device)
-                          for kp in k_pos_host]
+        self.plans = [torch.from_numpy(cpattn_varlen_plan(q_pos_host, kp, cu_host, hq, hkv, d, dt)).to(self.q.device)
+                      for kp in k_pos_host]
 
     def call_block(self, b, o, lse, accumulate):
         if self.cu_seqlens is not None:
             cpattn_varlen_partial(self.q, self.k_blocks[b], self.v_blocks[b], self.q_pos, self.k_pos_blocks[b],
                                   self.cu_seqlens, o, lse, accumulate=accumulate,
-                                  wg_order=None if self.wg_orders is None else self.wg_orders[b])
+                                  plan=None if self.plans is None else self.plans[b])
         else:
             cpattn_partial(self.q, self.k_blocks[b], self.v_blocks[b], self.q_pos, self.k_pos_blocks[b], o, lse,
                            causal=self.causal, accumulate=accumulate)
@@ -143,7 +143,7 @@ class RankShare:
 def share_from_workload(wl, device="cuda", blocks=None, plan=True):
     """Build a RankShare for a synth.Workload: positions from the library's
     index builder, tensors from the seeded generators; with documents (and
-    `plan`), the planned dispatch order of every block's call."""
+    `plan`), the plan of every block's call."""
     import torch
     docs = wl.doc_lens()
     cu = None if docs is None else np.concatenate([[0], np.cumsum(docs)]).astype(np.int32)
@@ -159,5 +159,5 @@ def share_from_workload(wl, device="cuda", blocks=None, plan=True):
     share.k_pos_host = [kps[b] for b in blocks]
     share.cu_host = cu
     if cu is not None and plan:
-        share.plan_orders(q_pos, share.k_pos_host, cu)
+        share.plan_blocks(q_pos, share.k_pos_host, cu)
     return share

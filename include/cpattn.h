@@ -149,49 +149,62 @@ cpattn_status cpattn_varlen_partial(const void *q, const void *k, const void *v,
 
 /*
  * Workgroups that one cpattn_partial / cpattn_varlen_partial call launches for
- * these sizes: the length of a dispatch order. -1 if the sizes are invalid
- * (lq < 0, hq or hkv < 1, hq % hkv != 0).
+ * these sizes (a plan holds one record per workgroup). -1 if the sizes are
+ * invalid (lq < 0, hq or hkv < 1, hq % hkv != 0).
  */
 int64_t cpattn_partial_workgroups(int64_t lq, int32_t hq, int32_t hkv);
 
+/* int32 entries per workgroup in a document call's plan (cpattn_varlen_plan). */
+#define CPATTN_VARLEN_PLAN_RECORD 48
+
 /*
- * HOST memory in and out. A dispatch order for cpattn_varlen_partial_ordered
- * on one KV block. With documents the work of a query tile depends on where
- * its rows sit inside their documents, not on their global position, so the
- * default heaviest-rows-first order leaves long tiles for the end of a launch.
- * This order keeps, for each of the 8 XCDs (workgroup id b runs on XCD b % 8),
- * the set of logical tiles the default order gives it (their K/V stays in that
- * XCD's L2) and puts them in decreasing order of the key tiles their
- * workgroup loads (ties by logical id): longest processing time first, so the
- * XCD's compute units finish close together. Positions and cu_seqlens as in
+ * HOST memory in and out. The plan of one document call (one KV block) for
+ * cpattn_varlen_partial_planned: one record of CPATTN_VARLEN_PLAN_RECORD int32
+ * per workgroup, opaque to the caller. A record holds the logical tile the
+ * workgroup computes and every range the kernel would otherwise search for at
+ * its start (its key range, and per wave the fully visible keys and the
+ * document starts of its first and last rows), so a planned workgroup starts
+ * with two dependent memory round trips instead of about seven. The order of
+ * the records is the dispatch order: with documents a query tile's work
+ * follows its place inside its documents, not its global position, so the
+ * default heaviest-rows-first order leaves long tiles for the end of a launch;
+ * the plan keeps, for each of the 8 XCDs (workgroup id b runs on XCD b % 8),
+ * the set of logical tiles the default order gives it (its K/V stays in that
+ * XCD's L2) and puts them in decreasing order of the key tiles they load
+ * (ties by logical id): longest processing time first. The method is the
+ * document masking of cpattn_varlen_partial (FCP page §3.2 and the Halo page's
+ * packing option); the plan only schedules it. Positions and cu_seqlens as in
  * cpattn_varlen_partial (ascending; checked here); in_dtype and head_dim as in
- * the call the order is for (they fix the key-tile size).
- *  order    receives n_order = cpattn_partial_workgroups(lq, hq, hkv) logical
- *           tile ids, a permutation of [0, n_order)
- * Errors: CPATTN_ERR_SHAPE (sizes, or n_order not the workgroup count),
- * CPATTN_ERR_NULL, CPATTN_ERR_DTYPE, CPATTN_ERR_UNSORTED. Deterministic.
+ * the call the plan is for (they fix the key-tile size).
+ *  plan      receives plan_len int32
+ *  plan_len  must be cpattn_partial_workgroups(lq, hq, hkv) x CPATTN_VARLEN_PLAN_RECORD
+ * Errors: CPATTN_ERR_SHAPE (sizes, or plan_len), CPATTN_ERR_NULL, CPATTN_ERR_DTYPE,
+ * CPATTN_ERR_UNSORTED. Deterministic; positions are fixed for a workload, so a
+ * caller plans each block once.
  */
 cpattn_status cpattn_varlen_plan(const int32_t *q_pos, int64_t lq, const int32_t *k_pos, int64_t lk,
                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
-                                 int32_t head_dim, cpattn_dtype in_dtype, int32_t *order, int64_t n_order);
+                                 int32_t head_dim, cpattn_dtype in_dtype, int32_t *plan, int64_t plan_len);
 
 /*
- * cpattn_varlen_partial with a caller's dispatch order: workgroup b computes
- * logical tile wg_order[b] (DEVICE memory, n_order int32 entries, 4-byte
- * aligned, n_order == cpattn_partial_workgroups(lq, hq, hkv)). Each logical
- * tile owns its rows, so any permutation gives results bit-identical to
- * cpattn_varlen_partial; only the time differs (cpattn_varlen_plan makes a
- * good one). Entries are clamped into [0, n_order): an order that is not a
- * permutation gives wrong results but no access outside the tensors (with
- * CPATTN_VALIDATE=1 it is rejected, CPATTN_ERR_RANGE, before any work). The
- * caller keeps wg_order alive until the call's work has finished on `stream`.
+ * cpattn_varlen_partial with a plan from cpattn_varlen_plan for exactly these
+ * positions, document offsets, sizes, in_dtype and head_dim: plan is DEVICE
+ * memory, 4-byte aligned, plan_len int32 as above; the caller keeps it alive
+ * until the call's work has finished on `stream`. Each logical tile owns its
+ * rows and the record's ranges are the ones the kernel's own searches find,
+ * so the results are bit-identical to cpattn_varlen_partial's in any record
+ * order. A plan made for other positions gives wrong results: every value in
+ * it that addresses memory is clamped into range in the kernel, so it never
+ * causes an access outside the tensors; with CPATTN_VALIDATE=1 the plan is
+ * recomputed on the host and a different one is rejected (CPATTN_ERR_RANGE)
+ * before any work.
  */
-cpattn_status cpattn_varlen_partial_ordered(const void *q, const void *k, const void *v, cpattn_dtype in_dtype,
+cpattn_status cpattn_varlen_partial_planned(const void *q, const void *k, const void *v, cpattn_dtype in_dtype,
                                             int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
                                             const int32_t *q_pos, const int32_t *k_pos,
                                             const int32_t *cu_seqlens, int32_t n_seqs, float softmax_scale,
                                             void *o, cpattn_dtype o_dtype, float *lse, int32_t accumulate,
-                                            const int32_t *wg_order, int64_t n_order, void *stream);
+                                            const int32_t *plan, int64_t plan_len, void *stream);
 
 /*
  * Several KV blocks that have all arrived, folded into (o, lse) in ONE launch

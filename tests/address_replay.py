@@ -344,14 +344,19 @@ def fwd_workgroups(lq, hq, hkv):
     return ((lq + 32 * r_wg - 1) // (32 * r_wg)) * (hq // g_wg)
 
 
+PLAN_REC = 48  # int32 per workgroup in a document call's plan
+PLAN_TILE, PLAN_KB, PLAN_KE, PLAN_SLAST, PLAN_SFIRST, PLAN_FLO, PLAN_FHI, PLAN_FLAGS = 0, 1, 2, 4, 12, 20, 28, 36
+
+
 def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumulate, blocks, varlen=False,
-                   n_seqs=0, multi=False, ordered=False):
+                   n_seqs=0, multi=False, plan=None):
     """One launch of the partial-attention kernel. blocks: list of
     (k tensor, v tensor, k_pos array name, lk) — one for a single-block call.
-    Tensors: 'q', 'o', 'lse', 'q_pos', 'cu' (and 'wg_order' when `ordered`: a
-    caller's dispatch order, whose entries the kernel clamps into [0, n_wg),
-    so every logical tile replayed below covers whatever it holds). Returns
-    the K/V tiles loaded."""
+    Tensors: 'q', 'o', 'lse', 'q_pos', 'cu' (and 'wg_plan' with `plan`, the
+    int32 records of a planned document call: the kernel reads its record
+    instead of searching, and clamps every addressing value from it into
+    range, as modelled here, so the tiles it loads stay inside the block
+    whatever the plan holds). Returns the K/V tiles loaded."""
     c = FwdCfg(in_bf16, D)
     G = hq // hkv
     g_wg = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
@@ -361,8 +366,17 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
     if n_wg <= 0:
         return 0
     check_remap(n_wg)
-    if ordered and not multi:
-        mem.index("wg_order", np.arange(n_wg, dtype=np.int64), "wg_order[blockIdx]")
+    planned = plan is not None and varlen and not multi
+    if planned:
+        # every workgroup id reads its record's tile and key range, and each
+        # wave its own entries
+        bid = np.arange(n_wg, dtype=np.int64)
+        mem.index("wg_plan", (bid[:, None] * PLAN_REC + np.array([PLAN_TILE, PLAN_KB, PLAN_KE])).ravel(), "plan")
+        for f in (PLAN_SLAST, PLAN_SFIRST, PLAN_FLO, PLAN_FHI, PLAN_FLAGS):
+            mem.index("wg_plan", (bid[:, None] * PLAN_REC + f + np.arange(8)).ravel(), "plan, per wave")
+        # one grid row per workgroup id, computing its record's (clamped)
+        # tile: a plan that repeats a tile is replayed as it runs
+        recs = np.asarray(plan, np.int64).reshape(n_wg, PLAN_REC)
     deep = False  # (two-ahead staging sets are no longer used)
     osz = 2 if out_bf16 else 4
     row_stride = hkv * D * c.esz
@@ -371,6 +385,8 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
 
     # grid: [workgroup, wave] (lanes on a last axis where they differ)
     L = np.arange(n_wg, dtype=np.int64)[:, None]
+    if planned:
+        L = np.clip(recs[:, PLAN_TILE], 0, n_wg - 1)[:, None]
     w = np.arange(8, dtype=np.int64)[None, :]
     hgrp = L // n_qtiles
     qt = n_qtiles - 1 - L % n_qtiles
@@ -389,7 +405,12 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
     if causal:
         mem.index("q_pos", qi, "q_pos[qi]")
     s_wg = s_wave = np.zeros(r0.shape, np.int64)
-    if varlen and causal:
+    if planned:
+        per_lane = recs[:, PLAN_FLAGS:PLAN_FLAGS + 8] & 1
+        across = per_lane.astype(bool)
+        if across.any():
+            sr.doc_start("cu", n_seqs, qp[qi[across]])
+    elif varlen and causal:
         i_first = np.where(active, r0, wg_r1 - 1)
         i_last = np.where(active, r1 - 1, wg_r1 - 1)
         mem.index("q_pos", np.stack([wg_r0, i_first, i_last]))
@@ -410,7 +431,11 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
     for (kt, vt, kp, lk) in blocks:
         kbase = hk * D * c.esz
         alive = ~exited
-        if causal and lk > 0:
+        if planned:
+            p_kb = np.broadcast_to(np.clip(recs[:, PLAN_KB], 0, lk)[:, None], r0.shape)
+            p_ke = np.broadcast_to(np.clip(recs[:, PLAN_KE], 0, lk)[:, None], r0.shape)
+            none = ~(p_ke > p_kb)
+        elif causal and lk > 0:
             mem.index(kp, [0, lk - 1], "kpos[0], kpos[lk - 1]")  # (a single-block call reads them first)
             mem.index("q_pos", wg_r1 - 1)
             none = sr.arrays[kp][0] > qp[wg_r1 - 1]
@@ -446,12 +471,16 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
                 load_positions(mem, psrc, (t0[m2] + 2) * c.BK, lk, wv, c.BK)
                 load_tile(mem, c, vt, hb[m1], row_stride, (t0[m1] + 1) * c.BK, lk, wv, True)
 
-        early = not varlen
+        early = not varlen or planned
         zeros = np.zeros(r0.shape, np.int64)
-        if early:
+        if planned:
+            load_first(act, p_kb // c.BK, (p_ke + c.BK - 1) // c.BK - p_kb // c.BK)
+        elif early:
             load_first(act, zeros, zeros + (lk + c.BK - 1) // c.BK)
         kb, ke = zeros, zeros + lk
-        if causal and act.any():
+        if planned:
+            kb, ke = p_kb.astype(np.int64), p_ke.astype(np.int64)
+        elif causal and act.any():
             q_lo_i = np.where(active, r0, wg_r1 - 1)
             mem.index("q_pos", np.stack([wg_r1 - 1, q_lo_i])[:, act])
             wq_hi = qp[wg_r1 - 1].astype(np.int64)

@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
                           "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse", "cpattn_bwd_delta",
                           "cpattn_partial_bwd", "cpattn_partial_workgroups", "cpattn_varlen_plan",
-                          "cpattn_varlen_partial_ordered"}
+                          "cpattn_varlen_partial_planned"}
     for n in names:
         assert hasattr(lib, n), n
 

@@ -38,9 +38,9 @@ def _documents_share():
     return wl, cu, q_pos, kps
 
 
-def _fwd_mem(lq, hq, hkv, d, kps, cu=None, in_esz=2, out_esz=2, n_order=0):
+def _fwd_mem(lq, hq, hkv, d, kps, cu=None, in_esz=2, out_esz=2, plan_len=0):
     sizes = dict(q=lq * hq * d * in_esz, o=lq * hq * d * out_esz, lse=hq * lq * 4, q_pos=lq * 4, null=0,
-                 cu=0 if cu is None else len(cu) * 4, wg_order=n_order * 4)
+                 cu=0 if cu is None else len(cu) * 4, wg_plan=plan_len * 4)
     for b, kp in enumerate(kps):
         lk = len(kp)
         sizes.update({"k%d" % b: lk * hkv * d * in_esz, "v%d" % b: lk * hkv * d * in_esz, "kp%d" % b: lk * 4})
@@ -73,20 +73,41 @@ def test_documents_share_forward_block_calls(documents, with_documents):
     order, the first writing O and LSE, the others accumulating into them.
     With documents the kernel searches before loading its first tiles; the
     same blocks without documents take the path that requests Q and the
-    first three tiles before the searches. The document calls take a planned
-    dispatch order, as the share runs them."""
+    first three tiles before the searches. The document calls also run
+    planned, as the share runs them (the plan from the library's planner)."""
+    from context_long_sequence_amd import cpattn_varlen_plan
     wl, cu, q_pos, kps = documents
-    n_order = ar.fwd_workgroups(wl.lq, wl.hq, wl.hkv)
-    mem = _fwd_mem(wl.lq, wl.hq, wl.hkv, wl.d, kps, cu, n_order=n_order)
+    plan_len = ar.fwd_workgroups(wl.lq, wl.hq, wl.hkv) * ar.PLAN_REC
+    mem = _fwd_mem(wl.lq, wl.hq, wl.hkv, wl.d, kps, cu, plan_len=plan_len)
     sr = ar.Searches(mem, _arrays(q_pos, kps, cu))
     tiles = 0
-    for i, b in enumerate(wl.arrival()):
-        tiles += ar.replay_forward(mem, sr, lq=wl.lq, hq=wl.hq, hkv=wl.hkv, D=wl.d, in_bf16=True, out_bf16=True,
-                                   causal=True, accumulate=i > 0,
-                                   blocks=[("k%d" % b, "v%d" % b, "kp%d" % b, len(kps[b]))],
-                                   varlen=with_documents, n_seqs=len(cu) - 1, ordered=with_documents)
+    for planned in ((False, True) if with_documents else (False,)):
+        for i, b in enumerate(wl.arrival()):
+            plan = cpattn_varlen_plan(q_pos, kps[b], cu, wl.hq, wl.hkv, wl.d) if planned else None
+            tiles += ar.replay_forward(mem, sr, lq=wl.lq, hq=wl.hq, hkv=wl.hkv, D=wl.d, in_bf16=True,
+                                       out_bf16=True, causal=True, accumulate=i > 0,
+                                       blocks=[("k%d" % b, "v%d" % b, "kp%d" % b, len(kps[b]))],
+                                       varlen=with_documents, n_seqs=len(cu) - 1, plan=plan)
     _report("documents share forward (%s)" % ("documents" if with_documents else "no documents"), mem,
-            ", %d K/V tiles over 4 calls" % tiles)
+            ", %d K/V tiles over %d calls" % (tiles, 8 if with_documents else 4))
+    assert tiles > 0
+
+
+def test_documents_share_forward_with_a_wrong_plan(documents):
+    """A plan made for other positions (seeded random records: tile ids, key
+    ranges and flags far outside their ranges) stays inside every tensor: the
+    kernel clamps each addressing value it takes from a record."""
+    wl, cu, q_pos, kps = documents
+    n_wg = ar.fwd_workgroups(wl.lq, wl.hq, wl.hkv)
+    mem = _fwd_mem(wl.lq, wl.hq, wl.hkv, wl.d, kps, cu, plan_len=n_wg * ar.PLAN_REC)
+    sr = ar.Searches(mem, _arrays(q_pos, kps, cu))
+    rng = np.random.default_rng(7)
+    b = wl.arrival()[0]
+    plan = rng.integers(-2 ** 31, 2 ** 31 - 1, size=n_wg * ar.PLAN_REC, dtype=np.int64).astype(np.int32)
+    tiles = ar.replay_forward(mem, sr, lq=wl.lq, hq=wl.hq, hkv=wl.hkv, D=wl.d, in_bf16=True, out_bf16=True,
+                              causal=True, accumulate=True, blocks=[("k%d" % b, "v%d" % b, "kp%d" % b, len(kps[b]))],
+                              varlen=True, n_seqs=len(cu) - 1, plan=plan)
+    _report("documents share forward, random plan", mem, ", %d K/V tiles" % tiles)
     assert tiles > 0
 
 

@@ -1,12 +1,14 @@
-"""The dispatch order of the document calls (cpattn_varlen_plan).
+"""The plan of a document call (cpattn_varlen_plan).
 
-Host logic (CPU): the order is a permutation of the call's workgroups; each
-XCD (workgroup id b runs on XCD b % 8) keeps the set of logical tiles the
-kernel's default order gives it; within an XCD the tiles go in decreasing
-order of the key tiles their workgroup loads, ties by logical id. The work of
-a tile is recomputed here from the positions, and on a small case by brute
-force over keys. GPU: the ordered call gives bit-identical results to the
-default order (each logical tile owns its rows).
+Host logic (CPU): the records' tiles are a permutation of the call's
+workgroups; each XCD (workgroup id b runs on XCD b % 8) keeps the set of
+logical tiles the kernel's default order gives it; within an XCD the tiles go
+in decreasing order of the key tiles their workgroup loads, ties by logical
+id. Every field of every record (key range, per-wave fully visible keys,
+document starts, per-lane search flag) is recomputed here from the positions
+with numpy, and the work of a tile on a small case by brute force over keys.
+GPU: the planned call gives results bit-identical to the unplanned one, in
+the planned record order and in a random one.
 """
 import numpy as np
 import pytest
@@ -56,15 +58,61 @@ def _work(q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16):
     return np.where(k_pos[0] > last, 0, nt)
 
 
-def _check_plan(order, q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16):
+REC = cp.VARLEN_PLAN_RECORD
+TILE, KB, KE, SLAST, SFIRST, FLO, FHI, FLAGS = 0, 1, 2, 4, 12, 20, 28, 36
+
+
+def _fields(q_pos, k_pos, cu, lq, hq, hkv):
+    """Every record field by logical tile, recomputed with numpy searches."""
+    n_qtiles, units, r_wg = _geometry(lq, hq, hkv)
+    n = n_qtiles * units
+    g_wg = 8 // r_wg
+    L = np.arange(n, dtype=np.int64)
+    qt = n_qtiles - 1 - L % n_qtiles
+    wg_r0 = qt * 32 * r_wg
+    wg_r1 = np.minimum(wg_r0 + 32 * r_wg, lq)
+    lk = len(k_pos)
+    k_first = k_pos[0] if lk else 0
+    k_last = k_pos[-1] if lk else 0
+    start_of = lambda x: cu[np.maximum(np.searchsorted(cu, x, side="right") - 1, 0)]
+    didx = lambda x: np.searchsorted(cu, x, side="right")
+    rec = np.zeros((n, REC), np.int64)
+    rec[:, TILE] = L
+    wq_hi = q_pos[wg_r1 - 1]
+    sees = (lk > 0) & ~(k_first > wq_hi)
+    s_wg = start_of(q_pos[wg_r0])
+    kb = np.where(k_first >= s_wg, 0, np.searchsorted(k_pos, s_wg, side="left"))
+    ke = np.where(k_last <= wq_hi, lk, np.searchsorted(k_pos, wq_hi, side="right"))
+    rec[:, KB] = np.where(sees, kb, 0)
+    rec[:, KE] = np.where(sees, ke, 0)
+    for w in range(8):
+        r0 = wg_r0 + 32 * (w // g_wg)
+        r1 = np.minimum(r0 + 32, lq)
+        act = r0 < lq
+        qf = np.where(act, q_pos[np.minimum(r0, lq - 1)], wq_hi)
+        ql = np.where(act, q_pos[np.maximum(r1 - 1, 0)], wq_hi)
+        sf, sl = start_of(qf), start_of(ql)
+        rec[:, SFIRST + w] = sf
+        rec[:, SLAST + w] = sl
+        rec[:, FLAGS + w] = (didx(ql) > didx(qf) + 1).astype(np.int64)
+        rec[:, FLO + w] = np.where(k_first >= sl, 0, np.searchsorted(k_pos, sl, side="left"))
+        rec[:, FHI + w] = np.where(k_last <= qf, lk, np.searchsorted(k_pos, qf, side="right"))
+    return rec
+
+
+def _check_plan(plan, q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16):
     n_qtiles, units, _ = _geometry(lq, hq, hkv)
     n = n_qtiles * units
-    assert len(order) == n == cp.cpattn_partial_workgroups(lq, hq, hkv)
+    assert len(plan) == n * REC and n == cp.cpattn_partial_workgroups(lq, hq, hkv)
+    recs = plan.reshape(n, REC).astype(np.int64)
+    order = recs[:, TILE]
     assert np.array_equal(np.sort(order), np.arange(n)), "not a permutation"
+    want = _fields(q_pos, k_pos, cu, lq, hq, hkv)
+    assert np.array_equal(recs, want[order]), "a record differs from its recomputation"
     work = _work(q_pos, k_pos, cu, lq, hq, hkv, d, in_bf16)
     default = _default_logical(n, units)
     for x in range(8):
-        ids = order[x::8].astype(np.int64)
+        ids = order[x::8]
         assert np.array_equal(np.sort(ids), np.sort(default[x::8])), "XCD %d's set changed" % x
         w = work[ids]
         assert np.all(np.diff(w) <= 0), "XCD %d: work not non-increasing" % x
@@ -100,11 +148,11 @@ def test_plan_keeps_xcd_sets_and_orders_by_work(S, cp_size, rank, hq, hkv, d, in
     kps = block_positions(S, cp_size, cp_size, "rank_shares", "zigzag", cu)
     lq = len(q_pos)
     for b, kp in enumerate(kps):
-        order = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d, "bf16" if in_bf16 else "f32")
-        work = _check_plan(order, q_pos, kp, cu, lq, hq, hkv, d, in_bf16)
+        plan = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d, "bf16" if in_bf16 else "f32")
+        work = _check_plan(plan, q_pos, kp, cu, lq, hq, hkv, d, in_bf16)
         assert work.max() > 0
         again = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d, "bf16" if in_bf16 else "f32")
-        assert np.array_equal(order, again), "the plan must be deterministic"
+        assert np.array_equal(plan, again), "the plan must be deterministic"
 
 
 def test_work_estimate_brute_force():
@@ -120,8 +168,8 @@ def test_work_estimate_brute_force():
     n_qtiles, units, r_wg = _geometry(len(q_pos), hq, hkv)
     BK = _tile_keys(True, d)
     for kp in kps:
-        order = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d)
-        work = _check_plan(order, q_pos, kp, cu, len(q_pos), hq, hkv, d, True)
+        plan = cp.cpattn_varlen_plan(q_pos, kp, cu, hq, hkv, d)
+        work = _check_plan(plan, q_pos, kp, cu, len(q_pos), hq, hkv, d, True)
         for L in range(n_qtiles * units):
             qt = n_qtiles - 1 - L % n_qtiles
             r0 = qt * 32 * r_wg
@@ -141,11 +189,11 @@ def test_plan_errors():
     k_pos = np.arange(256, dtype=np.int32)
     cu = np.array([0, 100, 256], np.int32)
     lib = cp.load_library()
-    n = cp.cpattn_partial_workgroups(256, 4, 4)
+    n = cp.cpattn_partial_workgroups(256, 4, 4) * REC
     out = np.zeros(n + 1, np.int32)
     st = lib.cpattn_varlen_plan(q_pos.ctypes.data, 256, k_pos.ctypes.data, 256, cu.ctypes.data, 2, 4, 4, 128, 0,
                                 out.ctypes.data, n + 1)
-    assert st == 2  # CPATTN_ERR_SHAPE: n_order is not the workgroup count
+    assert st == 2  # CPATTN_ERR_SHAPE: plan_len is not workgroups x the record size
     bad = q_pos[::-1].copy()
     with pytest.raises(cp.CpattnError) as e:
         cp.cpattn_varlen_plan(bad, k_pos, cu, 4, 4, 128)
@@ -159,24 +207,28 @@ def test_plan_errors():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name", ["docs8k_zigzag_cp4_h4_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
-def test_ordered_calls_bit_identical(name):
-    """The share's planned dispatch orders, a random permutation and the
-    default order give bit-identical O and LSE (accumulate mode, every block)."""
+@pytest.mark.parametrize("name", ["docs8k_zigzag_cp4_h4_d128", "docs8k_zigzag_cp4_h4kv2_d64",
+                                  "docs4k_zigzag_cp4_h2kv1_d64_tiny"])
+def test_planned_calls_bit_identical(name):
+    """The share's plans, the same records in a random order and the unplanned
+    calls give bit-identical O and LSE (accumulate mode, every block)."""
     import torch
     from test_gpu_parity import _reduced, say
     from context_long_sequence_amd.share import share_from_workload
     wl = _reduced()[name]
-    say("%s: planned / random / default dispatch order" % name)
+    say("%s: planned / shuffled records / unplanned" % name)
     planned = share_from_workload(wl)
-    assert planned.wg_orders is not None
+    assert planned.plans is not None
     o1, l1 = [t.clone() for t in planned.step(wl.arrival())]
-    n = planned.wg_orders[0].numel()
     rng = np.random.default_rng(3)
-    planned.wg_orders = [torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda() for _ in planned.wg_orders]
+    shuffled = []
+    for pl in planned.plans:
+        recs = pl.view(-1, REC)
+        shuffled.append(recs[torch.from_numpy(rng.permutation(recs.shape[0])).cuda()].contiguous().view(-1))
+    planned.plans = shuffled
     o2, l2 = [t.clone() for t in planned.step(wl.arrival())]
     plain = share_from_workload(wl, plan=False)
-    assert plain.wg_orders is None
+    assert plain.plans is None
     o3, l3 = plain.step(wl.arrival())
     torch.cuda.synchronize()
     for o, l in ((o2, l2), (o3, l3)):

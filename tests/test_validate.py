@@ -1,5 +1,7 @@
 """CPATTN_VALIDATE=1: the calls copy the position arrays to the host and reject
-ones that do not ascend (CPATTN_ERR_UNSORTED) before anything is enqueued.
+ones that do not ascend (CPATTN_ERR_UNSORTED), and a planned document call
+recomputes its plan and rejects one made for other positions
+(CPATTN_ERR_RANGE), before anything is enqueued.
 The setting is read once per process, so the checks run in a child process
 started with it set."""
 import os
@@ -44,6 +46,12 @@ print("fwd q unsorted", status(lambda: cp.cpattn_partial(q, k, v, bad_q, kp, o, 
 print("fwd k unsorted", status(lambda: cp.cpattn_partial(q, k, v, qp, bad_k, o, lse)))
 print("varlen cu unsorted", status(lambda: cp.cpattn_varlen_partial(q, k, v, qp, kp, bad_cu, o, lse)))
 print("varlen sorted", status(lambda: cp.cpattn_varlen_partial(q, k, v, qp, kp, cu, o, lse)))
+plan = cp.cpattn_varlen_plan(qp.cpu().numpy(), kp.cpu().numpy(), cu.cpu().numpy(), hq, hq, d)
+other = cp.cpattn_varlen_plan(qp.cpu().numpy(), (kp + 7).cpu().numpy(), cu.cpu().numpy(), hq, hq, d)
+print("varlen plan", status(lambda: cp.cpattn_varlen_partial(q, k, v, qp, kp, cu, o, lse,
+                                                              plan=torch.from_numpy(plan).to(dev))))
+print("varlen other plan", status(lambda: cp.cpattn_varlen_partial(q, k, v, qp, kp, cu, o, lse,
+                                                                    plan=torch.from_numpy(other).to(dev))))
 cp.cpattn_partial(q, k, v, qp, kp, o, lse)
 delta = torch.empty((hq, lq), dtype=torch.float32, device=dev)
 cp.cpattn_bwd_delta(o, q, delta)
@@ -73,6 +81,8 @@ def test_validate_rejects_unsorted_positions():
         "fwd k unsorted": "ERR_UNSORTED",
         "varlen cu unsorted": "ERR_UNSORTED",
         "varlen sorted": "OK",
+        "varlen plan": "OK",
+        "varlen other plan": "ERR_RANGE",
         "bwd sorted": "OK",
         "bwd k unsorted": "ERR_UNSORTED",
         "bwd cu unsorted": "ERR_UNSORTED",
