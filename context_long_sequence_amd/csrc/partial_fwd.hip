@@ -725,7 +725,9 @@ __global__ __launch_bounds__(kThreads, 1) void partial_fwd_kernel(PartialParams 
       }
     }
     kt_begin = kb / BK;
-    nt = (ke + BK - 1) / BK - kt_begin;   // tiles this workgroup loads (>= 1 without documents)
+    // tiles this workgroup loads (>= 1 without documents; none when its rows'
+    // documents hold no key of the block, even off a tile boundary)
+    nt = ke > kb ? (ke + BK - 1) / BK - kt_begin : 0;
     if (nt <= 0) {
       // (with documents the rows may still see nothing; tiles are loaded early
       // only without documents, but never leave with loads into LDS in flight)

@@ -495,7 +495,7 @@ def replay_forward(mem, sr, *, lq, hq, hkv, D, in_bf16, out_bf16, causal, accumu
                 kb[s_kb] = sr.wave_upper_bound(kp, lk, s_wg[s_kb] - 1)
                 sr.wave_upper_bound(kp, lk, s_wave[act & ~(k_first >= s_wave)] - 1)
         kt_begin = kb // c.BK
-        nt = (ke + c.BK - 1) // c.BK - kt_begin
+        nt = np.where(ke > kb, (ke + c.BK - 1) // c.BK - kt_begin, 0)
         if not (np.all(kt_begin == kt_begin[:, :1]) and np.all(nt == nt[:, :1])):
             raise AccessError("waves of a workgroup disagree on its tile range")
         go = act & (nt > 0)
