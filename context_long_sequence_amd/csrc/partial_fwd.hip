@@ -70,7 +70,10 @@
 //    groups split evenly over the 8 XCDs, workgroup ids are remapped so that
 //    consecutive logical tiles (same KV head) run on the same XCD and share
 //    its L2; otherwise the hardware's round-robin order is kept, so that no
-//    XCD gets all the heaviest tiles.
+//    XCD gets all the heaviest tiles. A document call may run from a host
+//    plan (plan_varlen below): workgroup b then takes its logical tile (each
+//    XCD's tiles by decreasing work) and every range its start would search
+//    for from record b, and requests Q and its first tiles at once.
 //  * A multi-block call (several blocks that have all arrived) runs the same
 //    code in a loop over a table of blocks: each block gets its own
 //    emptiness test, searches and tile loop, while the running max, running
