@@ -428,6 +428,26 @@ def backward_step(wl, share, order, step_flops, steps, warmup, cpu_seconds=None)
                "mean_call_ms": round(call_ms, 5),
                "calls": n_call,
            }}
+    # beside it: the same step with every block's gradients in one
+    # cpattn_partial_bwd_multi call (dQ summed in registers, one grid of key
+    # workgroups over all blocks)
+    if len(order) > 1:
+        for _ in range(max(1, warmup)):
+            share.backward(dout, order, mode="fused")
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            share.backward(dout, order, mode="fused")
+        stop.record(stream)
+        torch.cuda.synchronize()
+        fms = start.elapsed_time(stop) / steps
+        ftf = bwd_flops / (fms * 1e-3) / 1e12
+        log("the same backward step as one multi-block call: %.3f ms/step, %.1f TFLOP/s algorithmic" % (fms, ftf))
+        out["multi_block_call"] = {"ms_per_step": round(fms, 4), "value": round(ftf, 2), "unit": "TFLOP/s",
+                                   "pct_of_peak": round(100.0 * ftf / peak, 2),
+                                   "entry_point": "cpattn_partial_bwd_multi", "headline": False}
+        share.backward(dout, order)  # the sample check below reads the per-block path's dq
+        torch.cuda.synchronize()
     if cpu_seconds:
         out["cpu_baseline"] = cpu_baseline_bwd(wl, share, dout_host, cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -16,6 +16,9 @@ Functions (same names as the C ABI):
   cpattn_bwd_delta(o, dout, delta)
   cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, causal=True, softmax_scale=0.0,
                      accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None)
+  cpattn_partial_bwd_multi(q, k_blocks, v_blocks, dout, q_pos, k_pos_blocks, lse, delta, dq, dk_blocks,
+                           dv_blocks, causal=True, softmax_scale=0.0, accumulate_dq=False, accumulate_dkv=False,
+                           cu_seqlens=None)
 
 Layouts: q, o [lq, hq, d]; k, v [lk, hkv, d]; lse [hq, lq] float32; positions
 int32 ascending. See include/cpattn.h for the full contract.
@@ -84,6 +87,9 @@ def load_library(path=LIB_PATH):
     lib.cpattn_partial_bwd.restype = ctypes.c_int
     lib.cpattn_partial_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32,
                                        f32, vp, vp, vp, i32, vp, vp, i32, vp]
+    lib.cpattn_partial_bwd_multi.restype = ctypes.c_int
+    lib.cpattn_partial_bwd_multi.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, vp, i32, i32, i32, i32, vp, vp, i32,
+                                             vp, i32, f32, vp, vp, vp, i32, vp, vp, i32, vp]
     lib.cpattn_merge_lse.restype = ctypes.c_int
     lib.cpattn_merge_lse.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp]
     if path == LIB_PATH:
@@ -340,7 +346,61 @@ def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, caus
     _check(lib, st)
 
 
+def cpattn_partial_bwd_multi(q, k_blocks, v_blocks, dout, q_pos, k_pos_blocks, lse, delta, dq, dk_blocks, dv_blocks,
+                             causal=True, softmax_scale=0.0, accumulate_dq=False, accumulate_dkv=False,
+                             cu_seqlens=None, stream=None):
+    """Gradients of several present KV blocks in one call, in list order: dq
+    (+)= the sum of the blocks' shares, dk_blocks[b], dv_blocks[b] (+)= block
+    b's key gradients; see cpattn_partial_bwd_multi in include/cpattn.h."""
+    import torch
+    lib = load_library()
+    n = len(k_blocks)
+    if n == 0 or len(v_blocks) != n or len(k_pos_blocks) != n or len(dk_blocks) != n or len(dv_blocks) != n:
+        raise CpattnError(5, "k_blocks, v_blocks, k_pos_blocks, dk_blocks and dv_blocks must be non-empty lists "
+                             "of one length")
+    if q.dim() != 3 or tuple(dout.shape) != tuple(q.shape):
+        raise CpattnError(2, "q, dout must be [lq, hq, d]")
+    lq, hq, d = q.shape
+    if tuple(lse.shape) != (hq, lq) or tuple(delta.shape) != (hq, lq):
+        raise CpattnError(2, "lse and delta must be [hq, lq]")
+    if tuple(dq.shape) != (lq, hq, d):
+        raise CpattnError(2, "dq must be [lq, hq, d]")
+    if dout.dtype != q.dtype:
+        raise CpattnError(3, "q, k, v and dout must share one dtype")
+    hkv = k_blocks[0].shape[1] if k_blocks[0].dim() == 3 else -1
+    for k, v, p, dk, dv in zip(k_blocks, v_blocks, k_pos_blocks, dk_blocks, dv_blocks):
+        if k.dim() != 3 or k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
+            raise CpattnError(2, "each k, v must be [lk, hkv, d] with q's d")
+        # (one KV head count for every block: the C ABI sizes each block's rows with it)
+        if k.shape[1] != hkv:
+            raise CpattnError(2, "every KV block must have the same number of KV heads (%d and %d)" % (hkv, k.shape[1]))
+        if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+            raise CpattnError(2, "each dk, dv must have its k's shape")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise CpattnError(3, "q, k, v and dout must share one dtype")
+        _pos_len(p, k.shape[0], "k_pos")
+    _pos_len(q_pos, lq, "q_pos")
+    ptrs = ctypes.c_void_p * n
+    kp = ptrs(*[_dev(k, "k", q.dtype) for k in k_blocks])
+    vp_ = ptrs(*[_dev(v, "v", q.dtype) for v in v_blocks])
+    pp = ptrs(*[_dev(p, "k_pos", torch.int32) for p in k_pos_blocks])
+    dkp = ptrs(*[_dev(t, "dk", torch.float32) for t in dk_blocks])
+    dvp = ptrs(*[_dev(t, "dv", torch.float32) for t in dv_blocks])
+    lks = (ctypes.c_int64 * n)(*[int(k.shape[0]) for k in k_blocks])
+    st = lib.cpattn_partial_bwd_multi(_dev(q, "q"), ctypes.cast(kp, ctypes.c_void_p),
+                                      ctypes.cast(vp_, ctypes.c_void_p), _dev(dout, "dout"), _dtype_code(q), lq,
+                                      ctypes.cast(lks, ctypes.c_void_p), n, hq, hkv, d,
+                                      _dev(q_pos, "q_pos", torch.int32), ctypes.cast(pp, ctypes.c_void_p),
+                                      int(bool(causal)), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                                      0 if cu_seqlens is None else cu_seqlens.numel() - 1, float(softmax_scale),
+                                      _dev(lse, "lse", torch.float32), _dev(delta, "delta", torch.float32),
+                                      _dev(dq, "dq", torch.float32), int(bool(accumulate_dq)),
+                                      ctypes.cast(dkp, ctypes.c_void_p), ctypes.cast(dvp, ctypes.c_void_p),
+                                      int(bool(accumulate_dkv)), _stream(stream))
+    _check(lib, st)
+
+
 __all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_partial_multi",
            "cpattn_partial_workgroups", "cpattn_varlen_plan",
-           "cpattn_merge_lse", "cpattn_bwd_delta", "cpattn_partial_bwd", "cpattn_version",
+           "cpattn_merge_lse", "cpattn_bwd_delta", "cpattn_partial_bwd", "cpattn_partial_bwd_multi", "cpattn_version",
            "CpattnError", "load_library", "header_functions"]

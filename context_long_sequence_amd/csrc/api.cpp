@@ -381,12 +381,13 @@ cpattn_status cpattn_bwd_delta(const void* o, cpattn_dtype o_dtype, const void* 
   return ok();
 }
 
-cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, const void* dout, cpattn_dtype in_dtype,
-                                 int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
-                                 const int32_t* q_pos, const int32_t* k_pos, int32_t causal,
-                                 const int32_t* cu_seqlens, int32_t n_seqs, float softmax_scale, const float* lse,
-                                 const float* delta, float* dq, int32_t accumulate_dq, float* dk, float* dv,
-                                 int32_t accumulate_dkv, void* stream) {
+// Everything cpattn_partial_bwd checks before it enqueues (one block's arguments).
+static cpattn_status check_bwd_args(const void* q, const void* k, const void* v, const void* dout,
+                                    cpattn_dtype in_dtype, int64_t lq, int64_t lk, int32_t hq, int32_t hkv,
+                                    int32_t head_dim, const int32_t* q_pos, const int32_t* k_pos, int32_t causal,
+                                    const int32_t* cu_seqlens, int32_t n_seqs, float softmax_scale, const float* lse,
+                                    const float* delta, float* dq, int32_t accumulate_dq, float* dk, float* dv,
+                                    int32_t accumulate_dkv, hipStream_t s) {
   if (lq != 0 && (!q || !dout || !lse || !delta || !dq))
     return fail(CPATTN_ERR_NULL, "q, dout, lse, delta and dq must be non-NULL");
   if (lk != 0 && (!k || !v || !dk || !dv)) return fail(CPATTN_ERR_NULL, "k, v, dk and dv must be non-NULL");
@@ -431,13 +432,20 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
     for (int b = a + 1; b < 3; ++b)
       if (overlaps(outs[a], nout[a], outs[b], nout[b])) return fail(CPATTN_ERR_ALIAS, "dq, dk and dv must not overlap");
   }
-  hipStream_t s = (hipStream_t)stream;
   if (validate_env() && causal) {
     cpattn_status st = check_sorted_device(q_pos, lq, "q_pos", s);
     if (st == CPATTN_OK) st = check_sorted_device(k_pos, lk, "k_pos", s);
     if (st == CPATTN_OK && cu_seqlens) st = check_sorted_device(cu_seqlens, (int64_t)n_seqs + 1, "cu_seqlens", s);
     if (st != CPATTN_OK) return st;
   }
+  return CPATTN_OK;
+}
+
+static cpattn::BwdParams bwd_params(const void* q, const void* k, const void* v, const void* dout, int64_t lq,
+                                    int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                    const int32_t* k_pos, int32_t causal, const int32_t* cu_seqlens, int32_t n_seqs,
+                                    float softmax_scale, const float* lse, const float* delta, float* dq,
+                                    int32_t accumulate_dq, float* dk, float* dv, int32_t accumulate_dkv) {
   cpattn::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.dout = dout; p.lse = lse; p.delta = delta;
   p.dq = dq; p.dk = dk; p.dv = dv;
@@ -446,8 +454,93 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
   p.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.causal = causal; p.acc_dq = accumulate_dq; p.acc_dkv = accumulate_dkv;
+  return p;
+}
+
+cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, const void* dout, cpattn_dtype in_dtype,
+                                 int64_t lq, int64_t lk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 const int32_t* q_pos, const int32_t* k_pos, int32_t causal,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, float softmax_scale, const float* lse,
+                                 const float* delta, float* dq, int32_t accumulate_dq, float* dk, float* dv,
+                                 int32_t accumulate_dkv, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  cpattn_status st = check_bwd_args(q, k, v, dout, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, causal,
+                                    cu_seqlens, n_seqs, softmax_scale, lse, delta, dq, accumulate_dq, dk, dv,
+                                    accumulate_dkv, s);
+  if (st != CPATTN_OK) return st;
+  const cpattn::BwdParams p = bwd_params(q, k, v, dout, lq, lk, hq, hkv, head_dim, q_pos, k_pos, causal, cu_seqlens,
+                                         n_seqs, softmax_scale, lse, delta, dq, accumulate_dq, dk, dv, accumulate_dkv);
   hipError_t e = in_dtype == CPATTN_F32 ? cpattn::launch_bwd_f32(p, head_dim, cu_seqlens != nullptr, s)
                                          : cpattn::launch_bwd(p, head_dim, cu_seqlens != nullptr, s);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+cpattn_status cpattn_partial_bwd_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                                       const void* dout, cpattn_dtype in_dtype, int64_t lq, const int64_t* lk_blocks,
+                                       int32_t n_blocks, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       const int32_t* q_pos, const int32_t* const* k_pos_blocks, int32_t causal,
+                                       const int32_t* cu_seqlens, int32_t n_seqs, float softmax_scale,
+                                       const float* lse, const float* delta, float* dq, int32_t accumulate_dq,
+                                       float* const* dk_blocks, float* const* dv_blocks, int32_t accumulate_dkv,
+                                       void* stream) {
+  if (!k_blocks || !v_blocks || !lk_blocks || !k_pos_blocks || !dk_blocks || !dv_blocks)
+    return fail(CPATTN_ERR_NULL, "the block arrays must be non-NULL");
+  if (n_blocks < 1 || n_blocks > cpattn::kMaxBwdBlocks)
+    return fail(CPATTN_ERR_RANGE, "n_blocks must be in [1, %d], got %d", cpattn::kMaxBwdBlocks, n_blocks);
+  hipStream_t s = (hipStream_t)stream;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    cpattn_status st = check_bwd_args(q, k_blocks[b], v_blocks[b], dout, in_dtype, lq, lk_blocks[b], hq, hkv,
+                                      head_dim, q_pos, k_pos_blocks[b], causal, cu_seqlens, n_seqs, softmax_scale,
+                                      lse, delta, dq, accumulate_dq, dk_blocks[b], dv_blocks[b], accumulate_dkv, s);
+    if (st != CPATTN_OK) return st;
+  }
+  // A block's dk, dv must not overlap any other block's inputs or outputs
+  // (the key kernel writes them while other blocks' keys are still read).
+  const int64_t esz = dsize(in_dtype);
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    const size_t nkb = (size_t)lk_blocks[b] * hkv * head_dim;
+    for (int32_t c = 0; c < n_blocks; ++c) {
+      if (c == b) continue;
+      const size_t nkc = (size_t)lk_blocks[c] * hkv * head_dim;
+      const void* outs[] = {dk_blocks[b], dv_blocks[b]};
+      for (const void* o : outs)
+        if (overlaps(o, nkb * 4, k_blocks[c], nkc * esz) || overlaps(o, nkb * 4, v_blocks[c], nkc * esz) ||
+            overlaps(o, nkb * 4, dk_blocks[c], nkc * 4) || overlaps(o, nkb * 4, dv_blocks[c], nkc * 4) ||
+            (k_pos_blocks[c] && overlaps(o, nkb * 4, k_pos_blocks[c], (size_t)lk_blocks[c] * 4)))
+          return fail(CPATTN_ERR_ALIAS, "dk and dv of block %d overlap the buffers of block %d", b, c);
+    }
+  }
+  if (in_dtype == CPATTN_F32) {
+    // float32 inputs: the single-block kernels, one block after another
+    for (int32_t b = 0; b < n_blocks; ++b) {
+      const cpattn::BwdParams p =
+          bwd_params(q, k_blocks[b], v_blocks[b], dout, lq, lk_blocks[b], hq, hkv, head_dim, q_pos, k_pos_blocks[b],
+                     causal, cu_seqlens, n_seqs, softmax_scale, lse, delta, dq, b > 0 || accumulate_dq,
+                     dk_blocks[b], dv_blocks[b], accumulate_dkv);
+      hipError_t e = cpattn::launch_bwd_f32(p, head_dim, cu_seqlens != nullptr, s);
+      if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  }
+  cpattn::BwdBlocks bt{};
+  bt.n = n_blocks;
+  int64_t wg = 0;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    wg += (lk_blocks[b] + 127) / 128 * hkv;
+    if (wg >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "too many key tiles over the blocks (>= 2^31 workgroups)");
+    bt.wg_end[b] = (int32_t)wg;
+    bt.lk[b] = (int32_t)lk_blocks[b];
+    bt.k[b] = k_blocks[b];
+    bt.v[b] = v_blocks[b];
+    bt.k_pos[b] = k_pos_blocks[b];
+    bt.dk[b] = dk_blocks[b];
+    bt.dv[b] = dv_blocks[b];
+  }
+  const cpattn::BwdParams p = bwd_params(q, nullptr, nullptr, dout, lq, 0, hq, hkv, head_dim, q_pos, nullptr, causal,
+                                         cu_seqlens, n_seqs, softmax_scale, lse, delta, dq, accumulate_dq, nullptr,
+                                         nullptr, accumulate_dkv);
+  hipError_t e = cpattn::launch_bwd_multi(p, bt, head_dim, cu_seqlens != nullptr, s);
   if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -29,6 +29,26 @@ struct BwdParams {
   int32_t n_tiles, n_wg;      // set per kernel by launch_bwd
 };
 
+// The KV blocks of a multi-block gradient call, in order (bf16 kernels only).
+// The key kernel's grid covers every block's workgroups: block b takes
+// workgroups wg_end[b-1] .. wg_end[b]-1 (wg_end[-1] = 0). The query kernel
+// walks the blocks in order, dQ summed in registers across them.
+constexpr int kMaxBwdBlocks = 32;
+struct BwdBlocks {
+  int32_t n;
+  int32_t lk[kMaxBwdBlocks];
+  int32_t wg_end[kMaxBwdBlocks];
+  const void* k[kMaxBwdBlocks];
+  const void* v[kMaxBwdBlocks];
+  const int32_t* k_pos[kMaxBwdBlocks];
+  float* dk[kMaxBwdBlocks];
+  float* dv[kMaxBwdBlocks];
+};
+
+// Enqueue the key-gradient kernel over all blocks of `bt` (p's k, v, k_pos,
+// lk, dk, dv unused), then the query-gradient kernel over the blocks in order.
+hipError_t launch_bwd_multi(BwdParams p, const BwdBlocks& bt, int head_dim, bool varlen, hipStream_t stream);
+
 // Enqueue the key-gradient kernel (if lk > 0) then the query-gradient kernel (if lq > 0):
 // bf16 q, k, v, dout (partial_bwd.hip) or float32 ones (partial_bwd_f32.hip).
 hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream);

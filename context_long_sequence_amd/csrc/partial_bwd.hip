@@ -187,8 +187,8 @@ __device__ __forceinline__ void store_rows_lds(float* out, int64_t row_stride, i
 
 constexpr int kDkvThreads = 512;   // four producer and four consumer waves
 
-template <int D, bool VARLEN>
-__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+template <int D, bool VARLEN, bool MULTI>
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p, BwdBlocks bt) {
   using T = BwdTile<D>;
   constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
   constexpr int NS = 4;                     // LDS stages of query tiles
@@ -211,7 +211,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const bool producer = wave < 4;
   const int kw = wave & 3;                  // the wave's 32-key block
   const int g = lane >> 5, li = lane & 31;
-  const int L = tile_order(blockIdx.x, p.n_wg, p.hkv);
+  int bid = blockIdx.x;
+  if constexpr (MULTI) {
+    // the block whose range of workgroups holds this one (blocks without
+    // keys have empty ranges; the grid ends at the last block's end)
+    int b = 0;
+    while (b + 1 < bt.n && bid >= bt.wg_end[b]) ++b;
+    bid -= b ? bt.wg_end[b - 1] : 0;
+    p.k = bt.k[b];
+    p.v = bt.v[b];
+    p.k_pos = bt.k_pos[b];
+    p.dk = bt.dk[b];
+    p.dv = bt.dv[b];
+    p.lk = bt.lk[b];
+    p.n_tiles = (p.lk + 127) / 128;
+    p.n_wg = p.n_tiles * p.hkv;
+  }
+  const int L = tile_order(bid, p.n_wg, p.hkv);
   const int hk = L / p.n_tiles;
   const int kt = L % p.n_tiles;  // early keys (seen by the most rows) first
   const int G = p.hq / p.hkv;
@@ -501,8 +517,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Query kernel: dQ of 128 rows of one query head.
 
-template <int D, bool VARLEN>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
+template <int D, bool VARLEN, bool MULTI>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p, BwdBlocks bt) {
   using T = BwdTile<D>;
   constexpr int NQ = T::kNQ, NDT = T::kNDT, TB = T::kBytes;
   __shared__ __attribute__((aligned(1024))) char k_s0[TB], k_s1[TB], v_s0[TB], v_s1[TB];
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int h = L / p.n_tiles;
   const int qt = p.n_tiles - 1 - L % p.n_tiles;  // late rows (that see the most keys) first
   const int hk = h / (p.hq / p.hkv);
-  const int lq = p.lq, lk = p.lk;
+  const int lq = p.lq;
   const int wg_r0 = qt * 128, wg_r1 = min(wg_r0 + 128, lq);
   const int r0 = wg_r0 + 32 * wave;
   const int qi = min(r0 + li, lq - 1);              // this lane's row (clamped)
@@ -524,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   // Rows that see none of the block add nothing, and when accumulating dQ is
   // left as it is: the common case (the block's first key is after the
   // workgroup's last row) is decided by one load, before Q and dO are read.
-  if (p.acc_dq && (lk == 0 || (p.causal && p.k_pos[0] > p.q_pos[wg_r1 - 1]))) return;
+  if (!MULTI && p.acc_dq && (p.lk == 0 || (p.causal && p.k_pos[0] > p.q_pos[wg_r1 - 1]))) return;
 
   // the wave's rows: B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8_t qreg[NQ], dreg[NQ];
@@ -543,33 +559,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int32_t my_start = VARLEN ? doc_start(p.cu_seqlens, p.n_seqs, my_qpos) : 0;
   const int32_t wq_first = __builtin_amdgcn_readfirstlane(p.causal ? p.q_pos[min(r0, lq - 1)] : 0);  // rows ascend
 
-  // keys the workgroup's rows can see
-  int kb = 0, ke = lk;
-  if (p.causal) {
-    ke = wave_upper_bound(p.k_pos, lk, p.q_pos[wg_r1 - 1]);
-    if constexpr (VARLEN) kb = wave_upper_bound(p.k_pos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
-  }
-  const int nt = ke > kb ? (ke - kb + 31) / 32 : 0;
-  // (with documents the rows may still see nothing)
-  if (nt == 0 && p.acc_dq) return;
-
-  const int kv_stride = p.hkv * D * 2;
-  const char* kbase = (const char*)p.k + (int64_t)hk * D * 2;
-  const char* vbase = (const char*)p.v + (int64_t)hk * D * 2;
-  u32x4_t kr[T::kUnits], vr[T::kUnits];
-  int32_t pr = 0;
-  auto fetch = [&](int t) __attribute__((always_inline)) {
-    const int j0 = kb + 32 * t;
-    fetch_rows<D>(kr, kbase, kv_stride, j0, lk, tid);
-    fetch_rows<D>(vr, vbase, kv_stride, j0, lk, tid);
-    if (tid < 32) pr = (p.causal && j0 + tid < lk) ? p.k_pos[j0 + tid] : 0x7FFFFFFF;
-  };
-  auto commit = [&](int st) __attribute__((always_inline)) {
-    commit_rows<D>(st ? (char CPATTN_LDS*)k_s1 : (char CPATTN_LDS*)k_s0, kr, tid);
-    commit_rows<D>(st ? (char CPATTN_LDS*)v_s1 : (char CPATTN_LDS*)v_s0, vr, tid);
-    if (tid < 32) (st ? p_s1 : p_s0)[tid] = pr;
-  };
-
   int ra[NQ];
 #pragma unroll
   for (int ks = 0; ks < NQ; ++ks) ra[ks] = T::off(li, 2 * ks + g);
@@ -581,114 +570,158 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16_t{};
 
-  if (nt > 0) {
-    fetch(0);
-    commit(0);
-  }
-  // (likewise before the loop: the Q and dO loads are done once the first
-  // tile is committed, and with no tile the loop does not run)
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  phase_barrier();
-  for (int t = 0; t < nt; ++t) {
-    const int st = t & 1;
-    if (t + 1 < nt) fetch(t + 1);
-    const char CPATTN_LDS* kl = st ? (const char CPATTN_LDS*)k_s1 : (const char CPATTN_LDS*)k_s0;
-    const char CPATTN_LDS* vl = st ? (const char CPATTN_LDS*)v_s1 : (const char CPATTN_LDS*)v_s0;
-    const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
+  // The blocks in order (one for a single-block call); dQ is summed in the
+  // accumulators across them and stored once.
+  bool seen = false;
+  for (int blk = 0; blk < (MULTI ? bt.n : 1); ++blk) {
+    const int lk = MULTI ? bt.lk[blk] : p.lk;
+    const int32_t* kpos = MULTI ? bt.k_pos[blk] : p.k_pos;
+    const void* kptr = MULTI ? bt.k[blk] : p.k;
+    const void* vptr = MULTI ? bt.v[blk] : p.v;
+    if (MULTI && (lk == 0 || (p.causal && kpos[0] > p.q_pos[wg_r1 - 1]))) continue;
 
-    // (the products run at raised priority: the other workgroup's wave on the
-    // SIMD then issues its vector work around them rather than in their way)
-    __builtin_amdgcn_s_setprio(1);
-    // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query
-    // row), alternating so that neither chain waits on its own previous MFMA;
-    // operands read RING ahead
-    constexpr int RING = 4;
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-    {
-      constexpr int NM = 2 * NQ;
-      auto rd = [&](int m) __attribute__((always_inline)) {
-        return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? vl : kl) + ra[m >> 1]);
-      };
-      bf16x8_t a[RING];
-#pragma unroll
-      for (int m = 0; m < RING; ++m) a[m] = rd(m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], dreg[m >> 1], dp, 0, 0, 0);
-        else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], qreg[m >> 1], s, 0, 0, 0);
-        if (m + RING < NM) a[m % RING] = rd(m + RING);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    // keys the workgroup's rows can see
+    int kb = 0, ke = lk;
+    if (p.causal) {
+      ke = wave_upper_bound(kpos, lk, p.q_pos[wg_r1 - 1]);
+      if constexpr (VARLEN) kb = wave_upper_bound(kpos, lk, doc_start(p.cu_seqlens, p.n_seqs, p.q_pos[wg_r0]) - 1);
     }
+    const int nt = ke > kb ? (ke - kb + 31) / 32 : 0;
+    // (with documents the rows may still see nothing)
+    if constexpr (MULTI) {
+      if (nt == 0) continue;
+    } else {
+      if (nt == 0 && p.acc_dq) return;
+    }
+    seen = true;
 
-    __builtin_amdgcn_s_setprio(0);
-    // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile.
-    // Without documents, a tile of 32 keys inside the block that are all at
-    // or before the wave's first row is seen in full by every row of the wave
-    // (rows past the end have LSE +inf, so P = 0): no mask.
-    const int lim = min(lk - (kb + 32 * t), 32);
-    const bool full = lim == 32 && (!p.causal || (!VARLEN && __builtin_amdgcn_readfirstlane(pl[31]) <= wq_first));
-    uint32_t pd[8];
-    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-    auto dsoft = [&](auto masked) __attribute__((always_inline)) {
-      constexpr bool M = decltype(masked)::value;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        i32x4 k4 = {0, 0, 0, 0};
-        if (M && p.causal) k4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
-        float dv[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bool vis = true;
-          if constexpr (M) {
-            vis = 8 * rr + 4 * g + c < lim;
-            if (p.causal) {
-              vis = vis & (k4[c] <= my_qpos);
-              if (VARLEN) vis = vis & (k4[c] >= my_start);
-            }
-          }
-          const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -lse2)) : 0.f;
-          dv[c] = pv * (dp[4 * rr + c] - dlt);
-        }
-        pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
-        pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
-      }
+    const int kv_stride = p.hkv * D * 2;
+    const char* kbase = (const char*)kptr + (int64_t)hk * D * 2;
+    const char* vbase = (const char*)vptr + (int64_t)hk * D * 2;
+    u32x4_t kr[T::kUnits], vr[T::kUnits];
+    int32_t pr = 0;
+    auto fetch = [&](int t) __attribute__((always_inline)) {
+      const int j0 = kb + 32 * t;
+      fetch_rows<D>(kr, kbase, kv_stride, j0, lk, tid);
+      fetch_rows<D>(vr, vbase, kv_stride, j0, lk, tid);
+      if (tid < 32) pr = (p.causal && j0 + tid < lk) ? kpos[j0 + tid] : 0x7FFFFFFF;
     };
-    if (full) dsoft(std::false_type{});
-    else dsoft(std::true_type{});
+    auto commit = [&](int st) __attribute__((always_inline)) {
+      commit_rows<D>(st ? (char CPATTN_LDS*)k_s1 : (char CPATTN_LDS*)k_s0, kr, tid);
+      commit_rows<D>(st ? (char CPATTN_LDS*)v_s1 : (char CPATTN_LDS*)v_s0, vr, tid);
+      if (tid < 32) (st ? p_s1 : p_s0)[tid] = pr;
+    };
 
-    __builtin_amdgcn_s_setprio(1);
-    // dQ^T += K^T dS^T (K^T read transposed, RING ahead)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    {
-      constexpr int NM = 2 * NDT;  // (hf, dt)
-      const u32x4 bd[2] = {{pd[0], pd[1], pd[2], pd[3]}, {pd[4], pd[5], pd[6], pd[7]}};
-      auto rd = [&](int m) __attribute__((always_inline)) {
-        return read_tr(kl, ta0[m % NDT], ta8[m % NDT], m / NDT, T::kRowBytes);
-      };
-      bf16x8_t a[RING];
-#pragma unroll
-      for (int m = 0; m < RING; ++m) a[m] = rd(m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        acc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bd[m / NDT]),
-                                                               acc[m % NDT], 0, 0, 0);
-        if (m + RING < NM) a[m % RING] = rd(m + RING);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    if (nt > 0) {
+      fetch(0);
+      commit(0);
     }
-    __builtin_amdgcn_s_setprio(0);
-    if (t + 1 < nt) commit(st ^ 1);
-    // Nothing is in flight here (the commit waited for its loads). Saying so
-    // keeps the compiler's wait analysis exact across the conditional commit:
-    // otherwise it takes the skipped commit's loads as possibly pending and
-    // waits in the next tile's matrix products for the tile fetch just
-    // issued.
+    // (likewise before the loop: the Q and dO loads are done once the first
+    // tile is committed, and with no tile the loop does not run)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     phase_barrier();
+    for (int t = 0; t < nt; ++t) {
+      const int st = t & 1;
+      if (t + 1 < nt) fetch(t + 1);
+      const char CPATTN_LDS* kl = st ? (const char CPATTN_LDS*)k_s1 : (const char CPATTN_LDS*)k_s0;
+      const char CPATTN_LDS* vl = st ? (const char CPATTN_LDS*)v_s1 : (const char CPATTN_LDS*)v_s0;
+      const int32_t CPATTN_LDS* pl = st ? (const int32_t CPATTN_LDS*)p_s1 : (const int32_t CPATTN_LDS*)p_s0;
+
+      // (the products run at raised priority: the other workgroup's wave on the
+      // SIMD then issues its vector work around them rather than in their way)
+      __builtin_amdgcn_s_setprio(1);
+      // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys; column: this lane's query
+      // row), alternating so that neither chain waits on its own previous MFMA;
+      // operands read RING ahead
+      constexpr int RING = 4;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      {
+        constexpr int NM = 2 * NQ;
+        auto rd = [&](int m) __attribute__((always_inline)) {
+          return *(const bf16x8_t CPATTN_LDS*)(((m & 1) ? vl : kl) + ra[m >> 1]);
+        };
+        bf16x8_t a[RING];
+#pragma unroll
+        for (int m = 0; m < RING; ++m) a[m] = rd(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], dreg[m >> 1], dp, 0, 0, 0);
+          else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], qreg[m >> 1], s, 0, 0, 0);
+          if (m + RING < NM) a[m % RING] = rd(m + RING);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      __builtin_amdgcn_s_setprio(0);
+      // dS^T = P (dP - D); register r is key 8(r/4) + 4g + r%4 of the tile.
+      // Without documents, a tile of 32 keys inside the block that are all at
+      // or before the wave's first row is seen in full by every row of the wave
+      // (rows past the end have LSE +inf, so P = 0): no mask.
+      const int lim = min(lk - (kb + 32 * t), 32);
+      const bool full = lim == 32 && (!p.causal || (!VARLEN && __builtin_amdgcn_readfirstlane(pl[31]) <= wq_first));
+      uint32_t pd[8];
+      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+      auto dsoft = [&](auto masked) __attribute__((always_inline)) {
+        constexpr bool M = decltype(masked)::value;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          i32x4 k4 = {0, 0, 0, 0};
+          if (M && p.causal) k4 = *(const i32x4 CPATTN_LDS*)(pl + 8 * rr + 4 * g);
+          float dv[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bool vis = true;
+            if constexpr (M) {
+              vis = 8 * rr + 4 * g + c < lim;
+              if (p.causal) {
+                vis = vis & (k4[c] <= my_qpos);
+                if (VARLEN) vis = vis & (k4[c] >= my_start);
+              }
+            }
+            const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * rr + c], p.scale_log2, -lse2)) : 0.f;
+            dv[c] = pv * (dp[4 * rr + c] - dlt);
+          }
+          pd[2 * rr] = pack_bf16x2(dv[0], dv[1]);
+          pd[2 * rr + 1] = pack_bf16x2(dv[2], dv[3]);
+        }
+      };
+      if (full) dsoft(std::false_type{});
+      else dsoft(std::true_type{});
+
+      __builtin_amdgcn_s_setprio(1);
+      // dQ^T += K^T dS^T (K^T read transposed, RING ahead)
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      {
+        constexpr int NM = 2 * NDT;  // (hf, dt)
+        const u32x4 bd[2] = {{pd[0], pd[1], pd[2], pd[3]}, {pd[4], pd[5], pd[6], pd[7]}};
+        auto rd = [&](int m) __attribute__((always_inline)) {
+          return read_tr(kl, ta0[m % NDT], ta8[m % NDT], m / NDT, T::kRowBytes);
+        };
+        bf16x8_t a[RING];
+#pragma unroll
+        for (int m = 0; m < RING; ++m) a[m] = rd(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          acc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, bd[m / NDT]),
+                                                                 acc[m % NDT], 0, 0, 0);
+          if (m + RING < NM) a[m % RING] = rd(m + RING);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (t + 1 < nt) commit(st ^ 1);
+      // Nothing is in flight here (the commit waited for its loads). Saying so
+      // keeps the compiler's wait analysis exact across the conditional commit:
+      // otherwise it takes the skipped commit's loads as possibly pending and
+      // waits in the next tile's matrix products for the tile fetch just
+      // issued.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      phase_barrier();
+    }
   }
+  if (MULTI && !seen && p.acc_dq) return;
 
   // ---- store: lane holds row qi, head-dimension entries 32dt + 8rr + 4g + 0..3 ----
   // through the K/V stages, which no wave reads after the last barrier: wave w
@@ -733,11 +766,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* o, const voi
 
 template <int D, bool VARLEN>
 static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {
+  const BwdBlocks none{};
   if (p.lk > 0) {
     BwdParams a = p;
     a.n_tiles = (p.lk + 127) / 128;
     a.n_wg = a.n_tiles * p.hkv;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kDkvThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN, false>), dim3(a.n_wg), dim3(kDkvThreads), 0, stream, a, none);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -745,7 +779,26 @@ static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {
     BwdParams a = p;
     a.n_tiles = (p.lq + 127) / 128;
     a.n_wg = a.n_tiles * p.hq;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, VARLEN>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, VARLEN, false>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a, none);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// bt.wg_end must hold the running sums of (lk_b + 127) / 128 * hkv.
+template <int D, bool VARLEN>
+static hipError_t launch_bwd_multi_typed(BwdParams p, const BwdBlocks& bt, hipStream_t stream) {
+  const int32_t n_kwg = bt.n > 0 ? bt.wg_end[bt.n - 1] : 0;
+  if (n_kwg > 0) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, VARLEN, true>), dim3(n_kwg), dim3(kDkvThreads), 0, stream, p, bt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.lq > 0) {
+    BwdParams a = p;
+    a.n_tiles = (p.lq + 127) / 128;
+    a.n_wg = a.n_tiles * p.hq;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, VARLEN, true>), dim3(a.n_wg), dim3(kBwdThreads), 0, stream, a, bt);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -754,6 +807,12 @@ static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {
 hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream) {
   if (head_dim == 128) return varlen ? launch_bwd_typed<128, true>(p, stream) : launch_bwd_typed<128, false>(p, stream);
   return varlen ? launch_bwd_typed<64, true>(p, stream) : launch_bwd_typed<64, false>(p, stream);
+}
+
+hipError_t launch_bwd_multi(BwdParams p, const BwdBlocks& bt, int head_dim, bool varlen, hipStream_t stream) {
+  if (head_dim == 128)
+    return varlen ? launch_bwd_multi_typed<128, true>(p, bt, stream) : launch_bwd_multi_typed<128, false>(p, bt, stream);
+  return varlen ? launch_bwd_multi_typed<64, true>(p, bt, stream) : launch_bwd_multi_typed<64, false>(p, bt, stream);
 }
 
 template <int D>

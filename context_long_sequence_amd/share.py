@@ -8,8 +8,8 @@ the C ABI. This is the loop of the FCP page ("ä»Žå›ºå®šçŽ¯åˆ°è‡ªç”±æ‹“æ‰‘ï¼šFCPå
 """
 import numpy as np
 
-from . import (cpattn_bwd_delta, cpattn_merge_lse, cpattn_partial, cpattn_partial_bwd, cpattn_partial_multi,
-               cpattn_varlen_partial, cpattn_varlen_plan, cpattn_zigzag_index)
+from . import (cpattn_bwd_delta, cpattn_merge_lse, cpattn_partial, cpattn_partial_bwd, cpattn_partial_bwd_multi,
+               cpattn_partial_multi, cpattn_varlen_partial, cpattn_varlen_plan, cpattn_zigzag_index)
 
 
 def bits_to_device(a, device="cuda"):
@@ -115,13 +115,15 @@ class RankShare:
         return self.o, self.lse
 
 
-    def backward(self, dout, order, lse=None):
+    def backward(self, dout, order, lse=None, mode="blocks"):
         """Gradients of the step: dq [lq, hq, d] and per-block dk, dv [lk_b, hkv, d]
         (float32), with every block's backward run in `order`.
 
         Uses the merged (self.o, self.lse) of the last forward step (or `lse`):
-        D = <dO, O> once, then one cpattn_partial_bwd call per block, the first
-        writing dq and the others adding to it; each block's dk, dv are written.
+        D = <dO, O> once, then (mode "blocks") one cpattn_partial_bwd call per
+        block, the first writing dq and the others adding to it, or (mode
+        "fused") one cpattn_partial_bwd_multi call over the blocks in `order`;
+        each block's dk, dv are written.
         """
         import torch
         lq, hq, d = self.q.shape
@@ -133,6 +135,14 @@ class RankShare:
             self.dv = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in self.k_blocks]
         lse = self.lse if lse is None else lse
         cpattn_bwd_delta(self.o, dout, self.delta)
+        if mode == "fused":
+            cpattn_partial_bwd_multi(self.q, [self.k_blocks[b] for b in order], [self.v_blocks[b] for b in order],
+                                     dout, self.q_pos, [self.k_pos_blocks[b] for b in order], lse, self.delta,
+                                     self.dq, [self.dk[b] for b in order], [self.dv[b] for b in order],
+                                     causal=self.causal, cu_seqlens=self.cu_seqlens)
+            return self.dq, self.dk, self.dv
+        if mode != "blocks":
+            raise ValueError("mode must be 'blocks' or 'fused'")
         for i, b in enumerate(order):
             cpattn_partial_bwd(self.q, self.k_blocks[b], self.v_blocks[b], dout, self.q_pos, self.k_pos_blocks[b],
                                lse, self.delta, self.dq, self.dk[b], self.dv[b], causal=self.causal,

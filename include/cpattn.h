@@ -300,6 +300,37 @@ cpattn_status cpattn_partial_bwd(const void *q, const void *k, const void *v, co
                                  float *dq, int32_t accumulate_dq, float *dk, float *dv, int32_t accumulate_dkv,
                                  void *stream);
 
+/*
+ * The gradients of several KV blocks that are all present, in one call: the
+ * backward pass runs over the same blocks as the forward (PCP page, §2.3),
+ * and, as in cpattn_partial_multi, blocks may be present together (FCP page,
+ * §3.3). The result is that of cpattn_partial_bwd called on each block in
+ * the given order (the first call with accumulate_dq, the others adding to
+ * dq), up to rounding: dk, dv of every block come out bit for bit as from
+ * that call; dq is summed over the blocks in float32 registers and written
+ * (or added) once, where the per-block calls round and store it after every
+ * block. Two launches: one key-gradient grid over all blocks' keys, then one
+ * query-gradient grid whose workgroups walk the blocks in order.
+ *
+ *  k_blocks, v_blocks, k_pos_blocks, lk_blocks, n_blocks   as in cpattn_partial_multi
+ *                     (n_blocks 1..32)
+ *  dk_blocks, dv_blocks  HOST arrays of n_blocks DEVICE pointers: block b's
+ *                     dk, dv [lk_blocks[b]][hkv][head_dim] float32
+ * Every other argument is as in cpattn_partial_bwd, and each block is checked
+ * as a cpattn_partial_bwd call would check it. A block's dk and dv must not
+ * overlap another block's buffers either (CPATTN_ERR_ALIAS). float32 inputs
+ * run the single-block kernels block after block. The caller keeps ownership
+ * of every buffer; the host arrays are read before the call returns.
+ */
+cpattn_status cpattn_partial_bwd_multi(const void *q, const void *const *k_blocks, const void *const *v_blocks,
+                                       const void *dout, cpattn_dtype in_dtype, int64_t lq, const int64_t *lk_blocks,
+                                       int32_t n_blocks, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       const int32_t *q_pos, const int32_t *const *k_pos_blocks, int32_t causal,
+                                       const int32_t *cu_seqlens, int32_t n_seqs, float softmax_scale,
+                                       const float *lse, const float *delta, float *dq, int32_t accumulate_dq,
+                                       float *const *dk_blocks, float *const *dv_blocks, int32_t accumulate_dkv,
+                                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

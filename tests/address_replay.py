@@ -610,17 +610,14 @@ def staged_store_offsets(first_rows, n_rows, heads, head, D):
     return np.concatenate(out)
 
 
-def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False, acc_dkv=False):
-    """One cpattn_partial_bwd call: the key kernel, then the query kernel.
-    Tensors: 'q', 'dout', 'k', 'v', 'lse', 'delta', 'q_pos', 'k_pos', 'cu',
-    'dq', 'dk', 'dv'."""
+def _bwd_keys(mem, sr, names, *, lq, lk, hq, hkv, D, causal, varlen, n_seqs):
+    """The key kernel's workgroups of one block (block tensors named in `names`)."""
     G = hq // hkv
     kchunks = D // 8
     tb = 32 * 2 * D
     li, g = LANES & 31, LANES >> 5
-    NQ, NDT = D // 16, D // 32
-    qp, kpa = sr.arrays.get("q_pos"), sr.arrays.get("k_pos")
-
+    NQ = D // 16
+    kpa = sr.arrays.get(names["k_pos"])
     # ---- key kernel: workgroup = 128 keys of one KV head ----
     if lk > 0:
         n_tiles = (lk + 127) // 128
@@ -635,10 +632,10 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
         wg_j1 = np.minimum(wg_j0 + 128, lk)
         i_lo, i_hi = np.zeros(n_wg, np.int64), np.full(n_wg, lq, np.int64)
         if causal:
-            mem.index("k_pos", wg_j0, "k_pos[wg_j0]")
+            mem.index(names["k_pos"], wg_j0, "k_pos[wg_j0]")
             i_lo = sr.wave_upper_bound("q_pos", lq, kpa[wg_j0].astype(np.int64) - 1)
             if varlen:
-                mem.index("k_pos", wg_j1 - 1)
+                mem.index(names["k_pos"], wg_j1 - 1)
                 i_hi = sr.wave_upper_bound("q_pos", lq, sr.doc_end("cu", n_seqs, kpa[wg_j1 - 1]) - 1)
         nqt = np.where(i_hi > i_lo, (i_hi - i_lo + 31) // 32, 0)
         n_it = G * nqt
@@ -678,55 +675,70 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
         hk3 = hk[:, None, None]
         for ks in range(NQ):
             off = ((kj * hkv + hk3) * D + 8 * g + 16 * ks) * 2
-            mem.plain("k", off, 16, "dkv kreg")
-            mem.plain("v", off, 16, "dkv vreg")
+            mem.plain(names["k"], off, 16, "dkv kreg")
+            mem.plain(names["v"], off, 16, "dkv vreg")
         if causal:
-            mem.index("k_pos", kj, "k_pos[kj]")
-            mem.index("k_pos", np.minimum(j0 + 31, lk - 1), "dkv wave's last key")
+            mem.index(names["k_pos"], kj, "k_pos[kj]")
+            mem.index(names["k_pos"], np.minimum(j0 + 31, lk - 1), "dkv wave's last key")
             if varlen:
                 sr.doc_end("cu", n_seqs, kpa[kj])
         # dK, dV leave through LDS (store_rows_lds): rows j0 + row, whole lines
         off = staged_store_offsets(j0, lk, hkv, hk[:, None], D)
-        mem.plain("dk", off, 16, "dk")
-        mem.plain("dv", off, 16, "dv")
+        mem.plain(names["dk"], off, 16, "dk")
+        mem.plain(names["dv"], off, 16, "dv")
 
-    # ---- query kernel: workgroup = 128 rows of one query head ----
-    if lq > 0:
-        n_tiles = (lq + 127) // 128
-        n_wg = n_tiles * hq
-        check_remap(n_wg)
-        kv_stride = hkv * D * 2
-        L = np.arange(n_wg, dtype=np.int64)
-        h = L // n_tiles
-        hk = h // G
-        wg_r0 = (n_tiles - 1 - L % n_tiles) * 128
-        wg_r1 = np.minimum(wg_r0 + 128, lq)
-        r0 = wg_r0[:, None] + 32 * np.arange(4, dtype=np.int64)[None, :]
-        qi = np.minimum(r0[..., None] + li, lq - 1)
-        row_valid = r0[..., None] + li < lq
-        h3 = h[:, None, None]
-        for ks in range(NQ):
-            off = ((qi * hq + h3) * D + 8 * g + 16 * ks) * 2
-            mem.plain("q", off, 16, "dq qreg")
-            mem.plain("dout", off, 16, "dq dreg")
-        mem.index("lse", h3 * lq + qi, "dq lse")
-        mem.index("delta", (h3 * lq + qi)[row_valid], "dq delta")
-        if causal:
-            mem.index("q_pos", qi, "dq q_pos")
-            mem.index("q_pos", np.minimum(r0, lq - 1), "dq wave's first row")
-            if varlen:
-                sr.doc_start("cu", n_seqs, qp[qi])
+
+
+def _bwd_query(mem, sr, blocks, *, lq, hq, hkv, D, causal, varlen, n_seqs, acc_dq, multi):
+    """The query kernel over `blocks` (a list of (names, lk)): a single-block
+    call (multi False, one block) or a multi-block call, whose workgroups walk
+    the blocks in order and store dQ once."""
+    G = hq // hkv
+    kchunks = D // 8
+    tb = 32 * 2 * D
+    li, g = LANES & 31, LANES >> 5
+    NQ = D // 16
+    qp = sr.arrays.get("q_pos")
+    n_tiles = (lq + 127) // 128
+    n_wg = n_tiles * hq
+    check_remap(n_wg)
+    kv_stride = hkv * D * 2
+    L = np.arange(n_wg, dtype=np.int64)
+    h = L // n_tiles
+    hk = h // G
+    wg_r0 = (n_tiles - 1 - L % n_tiles) * 128
+    wg_r1 = np.minimum(wg_r0 + 128, lq)
+    r0 = wg_r0[:, None] + 32 * np.arange(4, dtype=np.int64)[None, :]
+    qi = np.minimum(r0[..., None] + li, lq - 1)
+    row_valid = r0[..., None] + li < lq
+    h3 = h[:, None, None]
+    for ks in range(NQ):
+        off = ((qi * hq + h3) * D + 8 * g + 16 * ks) * 2
+        mem.plain("q", off, 16, "dq qreg")
+        mem.plain("dout", off, 16, "dq dreg")
+    mem.index("lse", h3 * lq + qi, "dq lse")
+    mem.index("delta", (h3 * lq + qi)[row_valid], "dq delta")
+    if causal:
+        mem.index("q_pos", qi, "dq q_pos")
+        mem.index("q_pos", np.minimum(r0, lq - 1), "dq wave's first row")
+        if varlen:
+            sr.doc_start("cu", n_seqs, qp[qi])
+    seen = np.zeros(n_wg, bool)
+    for names, lk in blocks:
+        kpn = names["k_pos"]
+        kpa = sr.arrays.get(kpn)
+        if multi and lk == 0:
+            continue  # the block is skipped before any read of it
         kb, ke = np.zeros(n_wg, np.int64), np.full(n_wg, lk, np.int64)
         if causal:
             mem.index("q_pos", np.stack([wg_r1 - 1, wg_r0]))
-            ke = sr.wave_upper_bound("k_pos", lk, qp[wg_r1 - 1])
+            ke = sr.wave_upper_bound(kpn, lk, qp[wg_r1 - 1])
             if varlen:
-                kb = sr.wave_upper_bound("k_pos", lk, sr.doc_start("cu", n_seqs, qp[wg_r0]) - 1)
+                kb = sr.wave_upper_bound(kpn, lk, sr.doc_start("cu", n_seqs, qp[wg_r0]) - 1)
         nt = np.where(ke > kb, (ke - kb + 31) // 32, 0)
-        if acc_dq and lk > 0 and causal:
-            mem.index("k_pos", [0], "k_pos[0]")
-        writes = ~((nt == 0) & bool(acc_dq))  # accumulating workgroups that see nothing leave dQ alone
-        mem.plain("dq", staged_store_offsets(r0[writes], lq, hq, h[writes][:, None], D), 16, "dq")
+        if (multi or acc_dq) and lk > 0 and causal:
+            mem.index(kpn, [0], "k_pos[0]")
+        seen |= nt > 0
         ts, own = ragged_ranges(np.zeros(n_wg), nt)  # fetch(0), then fetch(t+1) for t + 1 < nt
         j0 = kb[own] + 32 * ts
         rows = clamp_rows(lk - j0, 32)
@@ -734,12 +746,62 @@ def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs
         for u in range(D // 64):
             unit = tid + 256 * u
             voff = (unit // kchunks) * kv_stride + (unit % kchunks) * 16
-            mem.buffer("k", hk[own] * D * 2 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq fetch k")
-            mem.buffer("v", hk[own] * D * 2 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq fetch v")
+            mem.buffer(names["k"], hk[own] * D * 2 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq fetch k")
+            mem.buffer(names["v"], hk[own] * D * 2 + j0 * kv_stride, rows * kv_stride, voff, 16, "dq fetch v")
             mem.lds(bwd_off(unit // kchunks, unit % kchunks, D), 16, tb, "dq commit")
         if causal and ts.size:
             idx = j0[:, None] + np.arange(32)
-            mem.index("k_pos", idx[idx < lk], "dq k_pos")
+            mem.index(kpn, idx[idx < lk], "dq k_pos")
+    writes = ~(~seen & bool(acc_dq))  # accumulating workgroups that see nothing leave dQ alone
+    mem.plain("dq", staged_store_offsets(r0[writes], lq, hq, h[writes][:, None], D), 16, "dq")
+
+
+BWD_NAMES = {"k": "k", "v": "v", "k_pos": "k_pos", "dk": "dk", "dv": "dv"}
+
+
+def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False, acc_dkv=False):
+    """One cpattn_partial_bwd call: the key kernel, then the query kernel.
+    Tensors: 'q', 'dout', 'k', 'v', 'lse', 'delta', 'q_pos', 'k_pos', 'cu',
+    'dq', 'dk', 'dv'."""
+    if lk > 0:
+        _bwd_keys(mem, sr, BWD_NAMES, lq=lq, lk=lk, hq=hq, hkv=hkv, D=D, causal=causal, varlen=varlen,
+                  n_seqs=n_seqs)
+    if lq > 0:
+        _bwd_query(mem, sr, [(BWD_NAMES, lk)], lq=lq, hq=hq, hkv=hkv, D=D, causal=causal, varlen=varlen,
+                   n_seqs=n_seqs, acc_dq=acc_dq, multi=False)
+
+
+def bwd_block_names(b):
+    return {"k": "k%d" % b, "v": "v%d" % b, "k_pos": "kp%d" % b, "dk": "dk%d" % b, "dv": "dv%d" % b}
+
+
+def replay_backward_multi(mem, sr, *, lq, lks, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False):
+    """One cpattn_partial_bwd_multi call over blocks b = 0 .. len(lks)-1 (block
+    b's tensors 'k<b>', 'v<b>', 'kp<b>', 'dk<b>', 'dv<b>'; the rest as in
+    replay_backward): the key kernel's grid over every block's workgroups,
+    then the query kernel walking the blocks."""
+    n = len(lks)
+    wg_end = np.cumsum([(lk + 127) // 128 * hkv for lk in lks]).astype(np.int64)
+    total = int(wg_end[-1])
+    if total >= 1 << 31:
+        raise AccessError("key-kernel grid too large")
+    # each workgroup's block: the first b (b + 1 < n) with bid < wg_end[b]
+    bid = np.arange(total, dtype=np.int64)
+    blk = np.zeros(total, np.int64)
+    for b in range(n - 1):
+        blk += bid >= wg_end[b]
+    local = bid - np.where(blk > 0, wg_end[np.maximum(blk - 1, 0)], 0)
+    for b in range(n):
+        n_wg = (lks[b] + 127) // 128 * hkv
+        mine = np.sort(local[blk == b])
+        if not np.array_equal(mine, np.arange(n_wg)):
+            raise AccessError("block %d's workgroups are not exactly 0 .. %d" % (b, n_wg - 1))
+        if lks[b] > 0:
+            _bwd_keys(mem, sr, bwd_block_names(b), lq=lq, lk=lks[b], hq=hq, hkv=hkv, D=D, causal=causal,
+                      varlen=varlen, n_seqs=n_seqs)
+    if lq > 0:
+        _bwd_query(mem, sr, [(bwd_block_names(b), lks[b]) for b in range(n)], lq=lq, hq=hq, hkv=hkv, D=D,
+                   causal=causal, varlen=varlen, n_seqs=n_seqs, acc_dq=acc_dq, multi=True)
 
 
 def f32_off(row, chunk):

@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
                           "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse", "cpattn_bwd_delta",
                           "cpattn_partial_bwd", "cpattn_partial_workgroups", "cpattn_varlen_plan",
-                          "cpattn_varlen_partial_planned"}
+                          "cpattn_varlen_partial_planned", "cpattn_partial_bwd_multi"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -222,3 +222,39 @@ def test_status_table_matches_the_header():
     enum = text[text.index("typedef enum {"):text.index("} cpattn_status;")]
     pairs = {int(v): k for k, v in re.findall(r"CPATTN_(\w+)\s*=\s*(\d+)", enum)}
     assert pairs == cp.STATUS
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+def test_backward_multi_rejects(lib):
+    def arr(t, vals):
+        a = (t * len(vals))(*vals)
+        return a, ctypes.cast(a, ctypes.c_void_p).value
+
+    kb, kbp = arr(ctypes.c_void_p, [B, B + 0x1000])
+    vb, vbp = arr(ctypes.c_void_p, [C, C + 0x1000])
+    pb, pbp = arr(ctypes.c_void_p, [K, K + 0x1000])
+    dkb, dkbp = arr(ctypes.c_void_p, [DK, DK + 0x1000])
+    dvb, dvbp = arr(ctypes.c_void_p, [DV, DV + 0x1000])
+    lk, lkp = arr(ctypes.c_int64, [8, 8])
+
+    def call(n=2, k=kbp, lks=lkp, dks=dkbp, hd=64, dt=0, causal=1, cu=0, ns=0, dq=O, adq=0, adkv=0):
+        return lib.cpattn_partial_bwd_multi(A, k, vbp, DO, dt, 8, lks, n, 1, 1, hd, P, pbp, causal, cu, ns, 0.0, L,
+                                            DL, dq, adq, dks, dvbp, adkv, 0)
+    assert call(k=0) == STATUS["ERR_NULL"]                    # no block array
+    assert call(dks=0) == STATUS["ERR_NULL"]
+    assert call(n=0) == STATUS["ERR_RANGE"]                   # no block
+    assert call(n=33) == STATUS["ERR_RANGE"]                  # over the table size
+    assert call(hd=96) == STATUS["ERR_SHAPE"]                 # checked per block as cpattn_partial_bwd would
+    assert call(dt=7) == STATUS["ERR_DTYPE"]
+    assert call(causal=2) == STATUS["ERR_RANGE"]
+    assert call(adq=2) == STATUS["ERR_RANGE"]
+    assert call(cu=0x80000, ns=1, causal=0) == STATUS["ERR_RANGE"]   # documents need causal
+    bad_lk, bad_lkp = arr(ctypes.c_int64, [8, 1 << 31])
+    assert call(lks=bad_lkp) == STATUS["ERR_SHAPE"]           # the second block's length
+    assert call(dq=B + 0x1000 + 16) == STATUS["ERR_ALIAS"]    # dq overlaps the second block's k
+    # block 0's dk overlaps block 1's v (within one block's call this would be allowed to pass
+    # the single-block checks; across blocks it is caught)
+    dk2, dk2p = arr(ctypes.c_void_p, [C + 0x1000, DK + 0x1000])
+    assert call(dks=dk2p) == STATUS["ERR_ALIAS"]
+    dk3, dk3p = arr(ctypes.c_void_p, [DK, DK + 0x10])         # the blocks' dk overlap each other
+    assert call(dks=dk3p) == STATUS["ERR_ALIAS"]

@@ -145,6 +145,52 @@ def test_documents_share_backward(documents):
         _report("documents share backward, block %d" % b, mem)
 
 
+def _bwd_multi_mem(lq, lks, hq, hkv, d, cu=None):
+    sizes = dict(q=lq * hq * d * 2, dout=lq * hq * d * 2, lse=hq * lq * 4, delta=hq * lq * 4, q_pos=lq * 4, null=0,
+                 cu=0 if cu is None else len(cu) * 4, dq=lq * hq * d * 4)
+    for b, lk in enumerate(lks):
+        sizes.update({"k%d" % b: lk * hkv * d * 2, "v%d" % b: lk * hkv * d * 2, "kp%d" % b: lk * 4,
+                      "dk%d" % b: lk * hkv * d * 4, "dv%d" % b: lk * hkv * d * 4})
+    return ar.Mem(**sizes)
+
+
+def test_documents_share_backward_multi(documents):
+    """The gradients of the documents share's four blocks in one
+    cpattn_partial_bwd_multi call (key kernel over all blocks, query kernel
+    walking them), accumulating dQ and not."""
+    wl, cu, q_pos, kps = documents
+    order = list(wl.arrival())
+    lks = [len(kps[b]) for b in order]
+    for acc in (False, True):
+        mem = _bwd_multi_mem(wl.lq, lks, wl.hq, wl.hkv, wl.d, cu)
+        sr = ar.Searches(mem, _arrays(q_pos, [kps[b] for b in order], cu))
+        ar.replay_backward_multi(mem, sr, lq=wl.lq, lks=lks, hq=wl.hq, hkv=wl.hkv, D=wl.d, causal=True,
+                                 varlen=True, n_seqs=len(cu) - 1, acc_dq=acc)
+        _report("documents share multi-block backward (accumulate_dq %d)" % acc, mem)
+
+
+def test_multi_backward_blocks_of_every_size():
+    """A multi-block gradient call with an empty block, a one-key block, a
+    ragged block, a block no row sees and the 64K share's block shape, GQA,
+    causal with and without grouped heads, both head dims."""
+    rng = np.random.default_rng(5)
+    for d, hq, hkv in ((64, 6, 3), (128, 4, 1)):
+        lq = 301
+        qp = np.sort(rng.choice(5000, lq, replace=False)).astype(np.int32) + 1000
+        lks = [0, 1, 333, 64, 128]
+        kps = [np.sort(rng.choice(6000, n, replace=False)).astype(np.int32) + 500 for n in lks]
+        kps[3] = np.arange(9000, 9064, dtype=np.int32)   # after every row
+        for causal in (True, False):
+            mem = _bwd_multi_mem(lq, lks, hq, hkv, d)
+            sr = ar.Searches(mem, _arrays(qp, kps))
+            ar.replay_backward_multi(mem, sr, lq=lq, lks=lks, hq=hq, hkv=hkv, D=d, causal=causal, acc_dq=causal)
+    # a block length past its tensors is caught
+    with pytest.raises(ar.AccessError):
+        mem = _bwd_multi_mem(10, [40], 1, 1, 64)
+        sr = ar.Searches(mem, _arrays(np.arange(10, dtype=np.int32), [np.arange(40, dtype=np.int32)]))
+        ar.replay_backward_multi(mem, sr, lq=10, lks=[40 * 200], hq=1, hkv=1, D=64, causal=True)
+
+
 RAGGED = [(100, 77, 2, 1), (257, 300, 3, 3), (33, 1, 4, 2), (70, 130, 16, 1), (50, 40, 3, 1)]
 
 
