@@ -5,7 +5,7 @@ The GPU tests append one JSON record per comparison to $CPATTN_PARITY_LOG
 compared and prints, for each group, the number of cases, the largest error
 found and its tolerance:
 
-    python tests/parity_summary.py gpurun_out/parity_errors.jsonl > PARITY.md
+    python tests/parity_summary.py parity_errors.jsonl > PARITY.md
 """
 import json
 import sys
