@@ -45,6 +45,11 @@
 //    one XCD (shared L2) when the heads split evenly over the 8 XCDs (else
 //    the hardware's round-robin order spreads the heavy tiles); the tiles
 //    with the most work go first.
+//  * Several blocks present at once (MULTI): the key kernel's grid covers
+//    every block's workgroups (a workgroup finds its block in a table of
+//    running workgroup counts, then runs the per-block code unchanged), and
+//    the query kernel's workgroups walk the blocks in order, so dQ stays in
+//    the accumulators across them and is stored once.
 #include <type_traits>
 
 #include "device_common.hpp"
