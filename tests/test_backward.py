@@ -146,10 +146,12 @@ def _large(name):
                                   pytest.param("docs128k_zigzag_cp4_h32_d128", marks=pytest.mark.skip(
                                       reason="faulted the GPU with an earlier forward-kernel variant; "
                                              "cause not yet shown")),
-                                  "docs64k_zigzag_cp4_h32_d128", "zigzag1m_cp8_h32kv8_d128"])
+                                  "docs64k_zigzag_cp4_h32_d128", "zigzag1m_cp8_h32kv8_d128",
+                                  "contig128k_h16kv2_d64"])
 def test_backward_full_size_sampled(torch_cuda, orc, name):
     """Full-size workloads (the 64K-token zig-zag share, the 128K-token
-    documents share, the 1M-token GQA share) in the launch configuration the
+    documents share, the 1M-token GQA share, the 128K-token Ulysses head
+    share at d 64) in the launch configuration the
     benchmark times: dq on sampled rows against the oracle; dk, dv of every
     key through invariants that hold at any size (each row's dS sums to zero
     over its keys, so dK sums to zero over all keys of a KV head; each row's
