@@ -15,7 +15,8 @@ Functions (same names as the C ABI):
   cpattn_merge_lse(o_acc, lse_acc, o_part, lse_part)
   cpattn_bwd_delta(o, dout, delta)
   cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, causal=True, softmax_scale=0.0,
-                     accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None)
+                     accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None, plan=None)
+  cpattn_bwd_query_workgroups(lq, hq), cpattn_varlen_bwd_plan(q_pos, k_pos, cu_seqlens, hq, hkv)
   cpattn_partial_bwd_multi(q, k_blocks, v_blocks, dout, q_pos, k_pos_blocks, lse, delta, dq, dk_blocks,
                            dv_blocks, causal=True, softmax_scale=0.0, accumulate_dq=False, accumulate_dkv=False,
                            cu_seqlens=None)
@@ -76,6 +77,13 @@ def load_library(path=LIB_PATH):
     lib.cpattn_partial_workgroups.argtypes = [i64, i32, i32]
     lib.cpattn_varlen_plan.restype = ctypes.c_int
     lib.cpattn_varlen_plan.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, i32, ctypes.c_int, vp, i64]
+    lib.cpattn_bwd_query_workgroups.restype = ctypes.c_int64
+    lib.cpattn_bwd_query_workgroups.argtypes = [i64, i32]
+    lib.cpattn_varlen_bwd_plan.restype = ctypes.c_int
+    lib.cpattn_varlen_bwd_plan.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, vp, i64]
+    lib.cpattn_varlen_partial_bwd_planned.restype = ctypes.c_int
+    lib.cpattn_varlen_partial_bwd_planned.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp,
+                                                      vp, i32, f32, vp, vp, vp, i32, vp, vp, i32, vp, i64, vp]
     lib.cpattn_varlen_partial_planned.restype = ctypes.c_int
     lib.cpattn_varlen_partial_planned.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, i32, vp, vp, vp, i32,
                                                   f32, vp, ctypes.c_int, vp, i32, vp, i64, vp]
@@ -246,6 +254,29 @@ def cpattn_varlen_plan(q_pos, k_pos, cu_seqlens, hq, hkv, head_dim, in_dtype="bf
     return plan[:n]
 
 
+def cpattn_bwd_query_workgroups(lq, hq):
+    """Workgroups of the query-gradient kernel: the length of a backward plan."""
+    return int(load_library().cpattn_bwd_query_workgroups(int(lq), int(hq)))
+
+
+def cpattn_varlen_bwd_plan(q_pos, k_pos, cu_seqlens, hq, hkv):
+    """Plan of one document gradient call (cpattn_partial_bwd(..., plan=)) from
+    HOST positions and document offsets (numpy int32): the query kernel's
+    dispatch order, one int32 per workgroup."""
+    lib = load_library()
+    qp = np.ascontiguousarray(q_pos, np.int32)
+    kp = np.ascontiguousarray(k_pos, np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    n = cpattn_bwd_query_workgroups(len(qp), hq)
+    if n < 0:
+        raise CpattnError(2, "invalid sizes lq=%d hq=%d" % (len(qp), hq))
+    plan = np.zeros(max(n, 1), np.int32)
+    st = lib.cpattn_varlen_bwd_plan(qp.ctypes.data, len(qp), kp.ctypes.data if len(kp) else None, len(kp),
+                                    cu.ctypes.data, len(cu) - 1, int(hq), int(hkv), plan.ctypes.data, n)
+    _check(lib, st)
+    return plan[:n]
+
+
 def cpattn_partial_multi(q, k_blocks, v_blocks, q_pos, k_pos_blocks, o, lse, causal=True, softmax_scale=0.0,
                          accumulate=False, cu_seqlens=None, stream=None):
     """Fold several arrived KV blocks into (o, lse) in one launch, in list
@@ -313,11 +344,13 @@ def cpattn_bwd_delta(o, dout, delta, stream=None):
 
 
 def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, causal=True, softmax_scale=0.0,
-                       accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None, stream=None):
+                       accumulate_dq=False, accumulate_dkv=False, cu_seqlens=None, stream=None, plan=None):
     """Gradients of one KV block: dq (+)= this block's share, dk, dv (+)= the block's key gradients.
 
     q, dout [lq, hq, d] bf16; k, v [lk, hkv, d] bf16; lse, delta [hq, lq] float32 (the merged LSE of
-    the forward and cpattn_bwd_delta's output); dq [lq, hq, d], dk, dv [lk, hkv, d] float32.
+    the forward and cpattn_bwd_delta's output); dq [lq, hq, d], dk, dv [lk, hkv, d] float32. With
+    documents, `plan` (a device int32 tensor from cpattn_varlen_bwd_plan) selects the planned call
+    (cpattn_varlen_partial_bwd_planned); the results are the same bit for bit.
     """
     import torch
     lib = load_library()
@@ -335,6 +368,18 @@ def cpattn_partial_bwd(q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv, caus
         raise CpattnError(3, "q, k, v and dout must share one dtype")
     _pos_len(q_pos, lq, "q_pos")
     _pos_len(k_pos, lk, "k_pos")
+    if plan is not None:
+        if cu_seqlens is None:
+            raise CpattnError(1, "a plan is for calls with documents (cu_seqlens)")
+        st = lib.cpattn_varlen_partial_bwd_planned(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dtype_code(q), lq, lk, hq, hkv, d,
+            _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32), cu_seqlens.numel() - 1, float(softmax_scale),
+            _dev(lse, "lse", torch.float32), _dev(delta, "delta", torch.float32), _dev(dq, "dq", torch.float32),
+            int(bool(accumulate_dq)), _dev(dk, "dk", torch.float32), _dev(dv, "dv", torch.float32),
+            int(bool(accumulate_dkv)), _dev(plan, "plan", torch.int32), plan.numel(), _stream(stream))
+        _check(lib, st)
+        return
     st = lib.cpattn_partial_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dtype_code(q), lq, lk,
                                 hq, hkv, d, _dev(q_pos, "q_pos", torch.int32), _dev(k_pos, "k_pos", torch.int32),
                                 int(bool(causal)), _dev(cu_seqlens, "cu_seqlens", torch.int32),
@@ -401,6 +446,6 @@ def cpattn_partial_bwd_multi(q, k_blocks, v_blocks, dout, q_pos, k_pos_blocks, l
 
 
 __all__ = ["cpattn_zigzag_index", "cpattn_partial", "cpattn_varlen_partial", "cpattn_partial_multi",
-           "cpattn_partial_workgroups", "cpattn_varlen_plan",
+           "cpattn_partial_workgroups", "cpattn_varlen_plan", "cpattn_bwd_query_workgroups", "cpattn_varlen_bwd_plan",
            "cpattn_merge_lse", "cpattn_bwd_delta", "cpattn_partial_bwd", "cpattn_partial_bwd_multi", "cpattn_version",
            "CpattnError", "load_library", "header_functions"]

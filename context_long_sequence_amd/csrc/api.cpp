@@ -476,6 +476,92 @@ cpattn_status cpattn_partial_bwd(const void* q, const void* k, const void* v, co
   return ok();
 }
 
+int64_t cpattn_bwd_query_workgroups(int64_t lq, int32_t hq) {
+  if (lq < 0 || hq < 1) return -1;
+  return cpattn::bwd_query_workgroups(lq, hq);
+}
+
+cpattn_status cpattn_varlen_bwd_plan(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk,
+                                     const int32_t* cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                     int32_t* plan, int64_t plan_len) {
+  if (lq < 0 || lk < 0) return fail(CPATTN_ERR_SHAPE, "lq and lk must be >= 0");
+  if (lq >= (int64_t)1 << 31 || lk >= (int64_t)1 << 31) return fail(CPATTN_ERR_SHAPE, "lq and lk must be < 2^31");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(CPATTN_ERR_SHAPE, "hq must be a positive multiple of hkv (hq=%d, hkv=%d)", hq, hkv);
+  if (n_seqs < 1) return fail(CPATTN_ERR_SHAPE, "n_seqs must be >= 1, got %d", n_seqs);
+  const int64_t n = cpattn::bwd_query_workgroups(lq, hq);
+  if (plan_len != n)
+    return fail(CPATTN_ERR_SHAPE, "plan_len must be %lld (the query kernel's workgroups), got %lld", (long long)n,
+                (long long)plan_len);
+  if (n == 0) return ok();
+  if (!q_pos || !cu_seqlens || !plan || (lk > 0 && !k_pos))
+    return fail(CPATTN_ERR_NULL, "q_pos, k_pos, cu_seqlens and plan must be non-NULL");
+  for (int64_t i = 1; i < lq; ++i)
+    if (q_pos[i] < q_pos[i - 1]) return fail(CPATTN_ERR_UNSORTED, "q_pos is not ascending at index %lld", (long long)i);
+  for (int64_t i = 1; i < lk; ++i)
+    if (k_pos[i] < k_pos[i - 1]) return fail(CPATTN_ERR_UNSORTED, "k_pos is not ascending at index %lld", (long long)i);
+  for (int32_t i = 1; i <= n_seqs; ++i)
+    if (cu_seqlens[i] < cu_seqlens[i - 1])
+      return fail(CPATTN_ERR_UNSORTED, "cu_seqlens is not ascending at index %d", i);
+  cpattn::plan_bwd_query(q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, plan);
+  return ok();
+}
+
+// Optional check that a device backward plan is the one cpattn_varlen_bwd_plan
+// makes for these positions (synchronises `stream`).
+static cpattn_status check_bwd_plan_device(const int32_t* dplan, const int32_t* q_pos, int64_t lq,
+                                           const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                                           int32_t n_seqs, int32_t hq, hipStream_t stream) {
+  const int64_t n = cpattn::bwd_query_workgroups(lq, hq);
+  std::vector<int32_t> plan((size_t)n), qp((size_t)lq), kp((size_t)lk), cu((size_t)n_seqs + 1), want((size_t)n);
+  hipError_t e = hipMemcpyAsync(plan.data(), dplan, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(qp.data(), q_pos, sizeof(int32_t) * (size_t)lq, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && lk > 0)
+    e = hipMemcpyAsync(kp.data(), k_pos, sizeof(int32_t) * (size_t)lk, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * ((size_t)n_seqs + 1), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "reading the plan for validation: %s", hipGetErrorString(e));
+  cpattn::plan_bwd_query(qp.data(), lq, kp.data(), lk, cu.data(), n_seqs, hq, want.data());
+  for (int64_t i = 0; i < n; ++i)
+    if (plan[(size_t)i] != want[(size_t)i])
+      return fail(CPATTN_ERR_RANGE, "the plan differs from cpattn_varlen_bwd_plan's at entry %lld (%d, expected %d)",
+                  (long long)i, plan[(size_t)i], want[(size_t)i]);
+  return CPATTN_OK;
+}
+
+cpattn_status cpattn_varlen_partial_bwd_planned(const void* q, const void* k, const void* v, const void* dout,
+                                                cpattn_dtype in_dtype, int64_t lq, int64_t lk, int32_t hq,
+                                                int32_t hkv, int32_t head_dim, const int32_t* q_pos,
+                                                const int32_t* k_pos, const int32_t* cu_seqlens, int32_t n_seqs,
+                                                float softmax_scale, const float* lse, const float* delta, float* dq,
+                                                int32_t accumulate_dq, float* dk, float* dv, int32_t accumulate_dkv,
+                                                const int32_t* plan, int64_t plan_len, void* stream) {
+  if (!cu_seqlens) return fail(CPATTN_ERR_NULL, "cu_seqlens must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  cpattn_status st = check_bwd_args(q, k, v, dout, in_dtype, lq, lk, hq, hkv, head_dim, q_pos, k_pos, 1, cu_seqlens,
+                                    n_seqs, softmax_scale, lse, delta, dq, accumulate_dq, dk, dv, accumulate_dkv, s);
+  if (st != CPATTN_OK) return st;
+  const int64_t n = cpattn::bwd_query_workgroups(lq, hq);
+  if (plan_len != n)
+    return fail(CPATTN_ERR_SHAPE, "plan_len must be %lld (the query kernel's workgroups), got %lld", (long long)n,
+                (long long)plan_len);
+  if (n > 0 && !plan) return fail(CPATTN_ERR_NULL, "plan must be non-NULL");
+  if (!aligned(plan, 4)) return fail(CPATTN_ERR_ALIGN, "plan must be 4-byte aligned");
+  if (n > 0 && validate_env()) {
+    st = check_bwd_plan_device(plan, q_pos, lq, k_pos, lk, cu_seqlens, n_seqs, hq, s);
+    if (st != CPATTN_OK) return st;
+  }
+  cpattn::BwdParams p = bwd_params(q, k, v, dout, lq, lk, hq, hkv, head_dim, q_pos, k_pos, 1, cu_seqlens, n_seqs,
+                                   softmax_scale, lse, delta, dq, accumulate_dq, dk, dv, accumulate_dkv);
+  // (float32 inputs run their own kernels in the default order)
+  p.dq_order = (in_dtype == CPATTN_BF16 && n > 0) ? plan : nullptr;
+  hipError_t e = in_dtype == CPATTN_F32 ? cpattn::launch_bwd_f32(p, head_dim, true, s)
+                                         : cpattn::launch_bwd(p, head_dim, true, s);
+  if (e != hipSuccess) return fail(CPATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 cpattn_status cpattn_partial_bwd_multi(const void* q, const void* const* k_blocks, const void* const* v_blocks,
                                        const void* dout, cpattn_dtype in_dtype, int64_t lq, const int64_t* lk_blocks,
                                        int32_t n_blocks, int32_t hq, int32_t hkv, int32_t head_dim,

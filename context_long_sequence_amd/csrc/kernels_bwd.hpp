@@ -27,6 +27,7 @@ struct BwdParams {
   float scale, scale_log2;
   int32_t causal, acc_dq, acc_dkv;
   int32_t n_tiles, n_wg;      // set per kernel by launch_bwd
+  const int32_t* dq_order;    // query kernel: logical tile of each workgroup (a host plan), or NULL
 };
 
 // The KV blocks of a multi-block gradient call, in order (bf16 kernels only).
@@ -53,6 +54,16 @@ hipError_t launch_bwd_multi(BwdParams p, const BwdBlocks& bt, int head_dim, bool
 // bf16 q, k, v, dout (partial_bwd.hip) or float32 ones (partial_bwd_f32.hip).
 hipError_t launch_bwd(BwdParams p, int head_dim, bool varlen, hipStream_t stream);
 hipError_t launch_bwd_f32(BwdParams p, int head_dim, bool varlen, hipStream_t stream);
+
+// Workgroups of the query-gradient kernel (128 rows of one query head each).
+int64_t bwd_query_workgroups(int64_t lq, int32_t hq);
+
+// Host: the query kernel's dispatch order for a call with documents (all
+// arguments in host memory, already validated): for each XCD, the logical
+// tiles the default order gives it, those that load the most key tiles
+// first (ties by logical id); plan[b] = the logical tile of workgroup b.
+void plan_bwd_query(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                    int32_t n_seqs, int32_t hq, int32_t* plan);
 
 // Enqueue delta[h][i] = <dout[i][h], o[i][h]>.
 hipError_t launch_bwd_delta(const void* o, int o_bf16, const void* dout, int do_bf16, int64_t lq, int32_t hq,

@@ -50,7 +50,9 @@
 //    running workgroup counts, then runs the per-block code unchanged), and
 //    the query kernel's workgroups walk the blocks in order, so dQ stays in
 //    the accumulators across them and is stored once.
+#include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "device_common.hpp"
 #include "kernels_bwd.hpp"
@@ -533,7 +535,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p, Bwd
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, li = lane & 31;
-  const int L = tile_order(blockIdx.x, p.n_wg, p.hq);
+  // (a planned call: the host's order, clamped into range, so a wrong plan
+  // gives wrong results but no access outside the tensors)
+  const int L = (!MULTI && p.dq_order)
+                    ? __builtin_amdgcn_readfirstlane(min(max(p.dq_order[blockIdx.x], 0), p.n_wg - 1))
+                    : tile_order(blockIdx.x, p.n_wg, p.hq);
   const int h = L / p.n_tiles;
   const int qt = p.n_tiles - 1 - L % p.n_tiles;  // late rows (that see the most keys) first
   const int hk = h / (p.hq / p.hkv);
@@ -768,6 +774,37 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* o, const voi
 }
 
 // ---------------------------------------------------------------------------
+
+int64_t bwd_query_workgroups(int64_t lq, int32_t hq) { return (lq + 127) / 128 * hq; }
+
+void plan_bwd_query(const int32_t* q_pos, int64_t lq, const int32_t* k_pos, int64_t lk, const int32_t* cu_seqlens,
+                    int32_t n_seqs, int32_t hq, int32_t* plan) {
+  const int32_t n_tiles = (int32_t)((lq + 127) / 128);
+  const int32_t n_wg = n_tiles * hq;
+  // the kernel's searches: keys up to the tile's last row, from the start of
+  // its first row's document
+  auto upper = [](const int32_t* a, int64_t n, int32_t x) { return std::upper_bound(a, a + n, x) - a; };
+  std::vector<int32_t> work((size_t)n_tiles);
+  for (int32_t qt = 0; qt < n_tiles; ++qt) {
+    const int64_t r0 = (int64_t)qt * 128, r1 = std::min<int64_t>(r0 + 128, lq);
+    const int64_t ke = upper(k_pos, lk, q_pos[r1 - 1]);
+    const int64_t d = upper(cu_seqlens, (int64_t)n_seqs + 1, q_pos[r0]);   // documents whose start <= the row
+    const int32_t ds = cu_seqlens[std::max<int64_t>(d - 1, 0)];
+    const int64_t kb = upper(k_pos, lk, ds - 1);
+    work[(size_t)qt] = ke > kb ? (int32_t)((ke - kb + 31) / 32) : 0;
+  }
+  auto work_of = [&](int32_t L) { return work[(size_t)(n_tiles - 1 - L % n_tiles)]; };
+  std::vector<int32_t> ls;
+  for (int x = 0; x < 8; ++x) {
+    ls.clear();
+    for (int32_t b = x; b < n_wg; b += 8) ls.push_back(tile_order(b, n_wg, hq));
+    std::stable_sort(ls.begin(), ls.end(), [&](int32_t a, int32_t c) {
+      return work_of(a) != work_of(c) ? work_of(a) > work_of(c) : a < c;
+    });
+    size_t i = 0;
+    for (int32_t b = x; b < n_wg; b += 8) plan[b] = ls[i++];
+  }
+}
 
 template <int D, bool VARLEN>
 static hipError_t launch_bwd_typed(BwdParams p, hipStream_t stream) {

@@ -9,7 +9,8 @@ the C ABI. This is the loop of the FCP page ("ä»Žå›ºå®šçŽ¯åˆ°è‡ªç”±æ‹“æ‰‘ï¼šFCPå
 import numpy as np
 
 from . import (cpattn_bwd_delta, cpattn_merge_lse, cpattn_partial, cpattn_partial_bwd, cpattn_partial_bwd_multi,
-               cpattn_partial_multi, cpattn_varlen_partial, cpattn_varlen_plan, cpattn_zigzag_index)
+               cpattn_partial_multi, cpattn_varlen_bwd_plan, cpattn_varlen_partial, cpattn_varlen_plan,
+               cpattn_zigzag_index)
 
 
 def bits_to_device(a, device="cuda"):
@@ -55,6 +56,7 @@ class RankShare:
         self._o_part = None
         self._lse_part = None
         self.plans = None   # per-block plans of the document calls (plan_blocks)
+        self.bwd_plans = None   # and of their gradient calls
 
     @property
     def n_blocks(self):
@@ -69,6 +71,8 @@ class RankShare:
         dt = "bf16" if self.q.dtype == torch.bfloat16 else "f32"
         self.plans = [torch.from_numpy(cpattn_varlen_plan(q_pos_host, kp, cu_host, hq, hkv, d, dt)).to(self.q.device)
                       for kp in k_pos_host]
+        self.bwd_plans = [torch.from_numpy(cpattn_varlen_bwd_plan(q_pos_host, kp, cu_host, hq, hkv)).to(self.q.device)
+                          for kp in k_pos_host]
 
     def call_block(self, b, o, lse, accumulate):
         if self.cu_seqlens is not None:
@@ -114,7 +118,6 @@ class RankShare:
             raise ValueError(mode)
         return self.o, self.lse
 
-
     def backward(self, dout, order, lse=None, mode="blocks"):
         """Gradients of the step: dq [lq, hq, d] and per-block dk, dv [lk_b, hkv, d]
         (float32), with every block's backward run in `order`.
@@ -123,7 +126,8 @@ class RankShare:
         D = <dO, O> once, then (mode "blocks") one cpattn_partial_bwd call per
         block, the first writing dq and the others adding to it, or (mode
         "fused") one cpattn_partial_bwd_multi call over the blocks in `order`;
-        each block's dk, dv are written.
+        each block's dk, dv are written. With documents and plans
+        (plan_blocks), each per-block call is planned.
         """
         import torch
         lq, hq, d = self.q.shape
@@ -146,7 +150,8 @@ class RankShare:
         for i, b in enumerate(order):
             cpattn_partial_bwd(self.q, self.k_blocks[b], self.v_blocks[b], dout, self.q_pos, self.k_pos_blocks[b],
                                lse, self.delta, self.dq, self.dk[b], self.dv[b], causal=self.causal,
-                               accumulate_dq=i > 0, accumulate_dkv=False, cu_seqlens=self.cu_seqlens)
+                               accumulate_dq=i > 0, accumulate_dkv=False, cu_seqlens=self.cu_seqlens,
+                               plan=None if self.bwd_plans is None else self.bwd_plans[b])
         return self.dq, self.dk, self.dv
 
 

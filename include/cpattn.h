@@ -301,6 +301,54 @@ cpattn_status cpattn_partial_bwd(const void *q, const void *k, const void *v, co
                                  void *stream);
 
 /*
+ * Workgroups of the query-gradient kernel of a cpattn_partial_bwd call: the
+ * length of a plan for cpattn_varlen_partial_bwd_planned (one int32 per
+ * workgroup; 128 query rows of one query head each). -1 for invalid sizes.
+ */
+int64_t cpattn_bwd_query_workgroups(int64_t lq, int32_t hq);
+
+/*
+ * Host-side plan of a gradient call with documents (the backward of
+ * cpattn_varlen_partial; PCP page, §2.3, and the FCP page's load balance
+ * over variable-length sequences, §3.2). With documents, a query tile's work
+ * is the keys from its first row's document start to its last row, so the
+ * query kernel's position order leaves long tiles for the end of a launch.
+ * The plan is the query kernel's dispatch order: plan[b] is the logical tile
+ * workgroup b computes. For each XCD (workgroup b runs on XCD b % 8) it keeps
+ * the set of tiles the default order gives that XCD, ordered by the key tiles
+ * they load, most first (ties by tile id). The plan changes only the order,
+ * so planned and unplanned calls give bit-identical results.
+ *
+ *  q_pos [lq], k_pos [lk], cu_seqlens [n_seqs + 1]  HOST int32 arrays, ascending
+ *  plan  HOST int32 [plan_len], written; plan_len = cpattn_bwd_query_workgroups(lq, hq)
+ * Errors: CPATTN_ERR_SHAPE (sizes, plan_len), CPATTN_ERR_NULL, CPATTN_ERR_UNSORTED.
+ * A plan depends only on the positions, so it is made once per block.
+ */
+cpattn_status cpattn_varlen_bwd_plan(const int32_t *q_pos, int64_t lq, const int32_t *k_pos, int64_t lk,
+                                     const int32_t *cu_seqlens, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                     int32_t *plan, int64_t plan_len);
+
+/*
+ * cpattn_partial_bwd with documents (causal = 1, cu_seqlens DEVICE, required)
+ * and the query kernel dispatched in the order of `plan` (DEVICE int32
+ * [plan_len], from cpattn_varlen_bwd_plan for the same positions; caller
+ * owns it). Results are those of the unplanned call, bit for bit. Every
+ * tile id read from the plan is clamped into range, so a plan for other
+ * positions gives wrong results but no access outside the tensors; with
+ * CPATTN_VALIDATE=1 the call recomputes the plan on the host and rejects a
+ * different one (CPATTN_ERR_RANGE) before any work. float32 inputs run in
+ * the default order. Other arguments and errors as in cpattn_partial_bwd.
+ */
+cpattn_status cpattn_varlen_partial_bwd_planned(const void *q, const void *k, const void *v, const void *dout,
+                                                cpattn_dtype in_dtype, int64_t lq, int64_t lk, int32_t hq,
+                                                int32_t hkv, int32_t head_dim, const int32_t *q_pos,
+                                                const int32_t *k_pos, const int32_t *cu_seqlens, int32_t n_seqs,
+                                                float softmax_scale, const float *lse, const float *delta,
+                                                float *dq, int32_t accumulate_dq, float *dk, float *dv,
+                                                int32_t accumulate_dkv, const int32_t *plan, int64_t plan_len,
+                                                void *stream);
+
+/*
  * The gradients of several KV blocks that are all present, in one call: the
  * backward pass runs over the same blocks as the forward (PCP page, §2.3),
  * and, as in cpattn_partial_multi, blocks may be present together (FCP page,

@@ -689,10 +689,12 @@ def _bwd_keys(mem, sr, names, *, lq, lk, hq, hkv, D, causal, varlen, n_seqs):
 
 
 
-def _bwd_query(mem, sr, blocks, *, lq, hq, hkv, D, causal, varlen, n_seqs, acc_dq, multi):
+def _bwd_query(mem, sr, blocks, *, lq, hq, hkv, D, causal, varlen, n_seqs, acc_dq, multi, order=None):
     """The query kernel over `blocks` (a list of (names, lk)): a single-block
     call (multi False, one block) or a multi-block call, whose workgroups walk
-    the blocks in order and store dQ once."""
+    the blocks in order and store dQ once. `order`: a planned call's plan (the
+    logical tile of each workgroup, read with plain loads and clamped into
+    range), or None for the default order."""
     G = hq // hkv
     kchunks = D // 8
     tb = 32 * 2 * D
@@ -703,7 +705,14 @@ def _bwd_query(mem, sr, blocks, *, lq, hq, hkv, D, causal, varlen, n_seqs, acc_d
     n_wg = n_tiles * hq
     check_remap(n_wg)
     kv_stride = hkv * D * 2
-    L = np.arange(n_wg, dtype=np.int64)
+    if order is None:
+        L = np.arange(n_wg, dtype=np.int64)   # (the default order is a permutation: every tile once)
+    else:
+        order = np.asarray(order, np.int64)
+        if order.shape != (n_wg,):
+            raise AccessError("a plan of %d entries for %d workgroups" % (len(order), n_wg))
+        mem.index("dq_plan", np.arange(n_wg), "dq plan")
+        L = np.clip(order, 0, n_wg - 1)
     h = L // n_tiles
     hk = h // G
     wg_r0 = (n_tiles - 1 - L % n_tiles) * 128
@@ -759,16 +768,18 @@ def _bwd_query(mem, sr, blocks, *, lq, hq, hkv, D, causal, varlen, n_seqs, acc_d
 BWD_NAMES = {"k": "k", "v": "v", "k_pos": "k_pos", "dk": "dk", "dv": "dv"}
 
 
-def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False, acc_dkv=False):
-    """One cpattn_partial_bwd call: the key kernel, then the query kernel.
-    Tensors: 'q', 'dout', 'k', 'v', 'lse', 'delta', 'q_pos', 'k_pos', 'cu',
-    'dq', 'dk', 'dv'."""
+def replay_backward(mem, sr, *, lq, lk, hq, hkv, D, causal, varlen=False, n_seqs=0, acc_dq=False, acc_dkv=False,
+                    dq_order=None):
+    """One cpattn_partial_bwd call (cpattn_varlen_partial_bwd_planned with
+    `dq_order`, its plan, in tensor 'dq_plan'): the key kernel, then the query
+    kernel. Tensors: 'q', 'dout', 'k', 'v', 'lse', 'delta', 'q_pos', 'k_pos',
+    'cu', 'dq', 'dk', 'dv'."""
     if lk > 0:
         _bwd_keys(mem, sr, BWD_NAMES, lq=lq, lk=lk, hq=hq, hkv=hkv, D=D, causal=causal, varlen=varlen,
                   n_seqs=n_seqs)
     if lq > 0:
         _bwd_query(mem, sr, [(BWD_NAMES, lk)], lq=lq, hq=hq, hkv=hkv, D=D, causal=causal, varlen=varlen,
-                   n_seqs=n_seqs, acc_dq=acc_dq, multi=False)
+                   n_seqs=n_seqs, acc_dq=acc_dq, multi=False, order=dq_order)
 
 
 def bwd_block_names(b):

@@ -18,7 +18,9 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cpattn_version", "cpattn_last_error", "cpattn_zigzag_index", "cpattn_partial",
                           "cpattn_varlen_partial", "cpattn_partial_multi", "cpattn_merge_lse", "cpattn_bwd_delta",
                           "cpattn_partial_bwd", "cpattn_partial_workgroups", "cpattn_varlen_plan",
-                          "cpattn_varlen_partial_planned", "cpattn_partial_bwd_multi"}
+                          "cpattn_varlen_partial_planned", "cpattn_partial_bwd_multi",
+                          "cpattn_bwd_query_workgroups", "cpattn_varlen_bwd_plan",
+                          "cpattn_varlen_partial_bwd_planned"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -258,3 +260,19 @@ def test_backward_multi_rejects(lib):
     assert call(dks=dk2p) == STATUS["ERR_ALIAS"]
     dk3, dk3p = arr(ctypes.c_void_p, [DK, DK + 0x10])         # the blocks' dk overlap each other
     assert call(dks=dk3p) == STATUS["ERR_ALIAS"]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="argument-rejection checks use fake addresses; CPU only")
+def test_backward_planned_rejects(lib):
+    PL = 0xD0000
+
+    def call(cu=0x80000, ns=1, plan=PL, plan_len=2, lq=8, hd=64, adq=0):
+        return lib.cpattn_varlen_partial_bwd_planned(A, B, C, DO, 0, lq, 8, 2, 1, hd, P, K, cu, ns, 0.0, L, DL, O, adq,
+                                                     DK, DV, 0, plan, plan_len, 0)
+    assert call(cu=0) == STATUS["ERR_NULL"]                    # documents are required
+    assert call(plan_len=3) == STATUS["ERR_SHAPE"]             # 1 row tile x 2 heads = 2 workgroups
+    assert call(plan=0) == STATUS["ERR_NULL"]
+    assert call(plan=PL + 2) == STATUS["ERR_ALIGN"]
+    assert call(hd=96) == STATUS["ERR_SHAPE"]                  # checked as cpattn_partial_bwd would
+    assert call(ns=0) == STATUS["ERR_SHAPE"]
+    assert call(adq=2) == STATUS["ERR_RANGE"]

@@ -128,7 +128,7 @@ def _bwd_mem(lq, lk, hq, hkv, d, cu=None):
     return ar.Mem(q=lq * hq * d * 2, dout=lq * hq * d * 2, o=lq * hq * d * 2, k=lk * hkv * d * 2,
                   v=lk * hkv * d * 2, lse=hq * lq * 4, delta=hq * lq * 4, q_pos=lq * 4, k_pos=lk * 4, null=0,
                   cu=0 if cu is None else len(cu) * 4, dq=lq * hq * d * 4, dk=lk * hkv * d * 4,
-                  dv=lk * hkv * d * 4)
+                  dv=lk * hkv * d * 4, dq_plan=(lq + 127) // 128 * hq * 4)
 
 
 def test_documents_share_backward(documents):
@@ -189,6 +189,24 @@ def test_multi_backward_blocks_of_every_size():
         mem = _bwd_multi_mem(10, [40], 1, 1, 64)
         sr = ar.Searches(mem, _arrays(np.arange(10, dtype=np.int32), [np.arange(40, dtype=np.int32)]))
         ar.replay_backward_multi(mem, sr, lq=10, lks=[40 * 200], hq=1, hkv=1, D=64, causal=True)
+
+
+def test_documents_share_backward_planned(documents):
+    """The planned gradient calls of the documents share (the library's plans
+    of the query kernel's order), and one with a seeded random plan of values
+    outside the tiles, which the kernel clamps."""
+    from context_long_sequence_amd import cpattn_varlen_bwd_plan
+    wl, cu, q_pos, kps = documents
+    rng = np.random.default_rng(9)
+    for i, b in enumerate(wl.arrival()):
+        plan = cpattn_varlen_bwd_plan(q_pos, kps[b], cu, wl.hq, wl.hkv)
+        if i == 0:
+            plan = rng.integers(-5, len(plan) + 5, len(plan))
+        mem = _bwd_mem(wl.lq, len(kps[b]), wl.hq, wl.hkv, wl.d, cu)
+        sr = ar.Searches(mem, {"q_pos": q_pos, "k_pos": kps[b], "cu": cu})
+        ar.replay_backward(mem, sr, lq=wl.lq, lk=len(kps[b]), hq=wl.hq, hkv=wl.hkv, D=wl.d, causal=True,
+                           varlen=True, n_seqs=len(cu) - 1, acc_dq=i > 0, dq_order=plan)
+        _report("documents share planned backward, block %d%s" % (b, " (random plan)" if i == 0 else ""), mem)
 
 
 RAGGED = [(100, 77, 2, 1), (257, 300, 3, 3), (33, 1, 4, 2), (70, 130, 16, 1), (50, 40, 3, 1)]

@@ -234,3 +234,102 @@ def test_planned_calls_bit_identical(name):
     for o, l in ((o2, l2), (o3, l3)):
         assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
         assert torch.equal(l1, l)
+
+
+# ---------------------------------------------------------------------------
+# The plan of a document gradient call (cpattn_varlen_bwd_plan): the query
+# kernel's dispatch order.
+
+def _bwd_query_work(q_pos, k_pos, cu, lq, hq):
+    """Key tiles (32 keys) each logical tile of the query kernel loads: keys from
+    its first row's document start to its last row (128 rows of one head)."""
+    n_tiles = (lq + 127) // 128
+    L = np.arange(n_tiles * hq, dtype=np.int64)
+    qt = n_tiles - 1 - L % n_tiles
+    r0 = qt * 128
+    r1 = np.minimum(r0 + 128, lq)
+    start = cu[np.searchsorted(cu, q_pos[r0], side="right") - 1]
+    kb = np.searchsorted(k_pos, start, side="left")
+    ke = np.searchsorted(k_pos, q_pos[r1 - 1], side="right")
+    return np.where(ke > kb, (ke - kb + 31) // 32, 0)
+
+
+@pytest.mark.parametrize("S,cp_size,rank,hq,hkv", [
+    (131072, 4, 1, 32, 32),     # the documents share (heads split over the 8 XCDs)
+    (16384, 4, 2, 12, 4),       # 12 heads: the hardware's order
+])
+def test_bwd_plan_keeps_xcd_sets_and_orders_by_work(S, cp_size, rank, hq, hkv):
+    cu = _documents_share(S, cp_size, 13, 256, 8192)
+    q_pos, _ = cp.cpattn_zigzag_index(S, cp_size, rank, "zigzag", cu)
+    kps = block_positions(S, cp_size, cp_size, "rank_shares", "zigzag", cu)
+    lq = len(q_pos)
+    n = cp.cpattn_bwd_query_workgroups(lq, hq)
+    assert n == (lq + 127) // 128 * hq
+    default = _default_logical(n, hq)
+    for kp in kps:
+        plan = cp.cpattn_varlen_bwd_plan(q_pos, kp, cu, hq, hkv)
+        assert plan.shape == (n,)
+        assert np.array_equal(np.sort(plan), np.arange(n)), "the plan must be a permutation of the tiles"
+        work = _bwd_query_work(q_pos.astype(np.int64), kp.astype(np.int64), cu.astype(np.int64), lq, hq)
+        assert work.max() > 0
+        for x in range(8):
+            mine = plan[x::8]
+            assert np.array_equal(np.sort(mine), np.sort(default[x::8])), "each XCD keeps its set of tiles"
+            w = work[mine]
+            assert np.all((w[:-1] > w[1:]) | ((w[:-1] == w[1:]) & (mine[:-1] < mine[1:]))), \
+                "longest first, ties by tile id"
+        assert np.array_equal(plan, cp.cpattn_varlen_bwd_plan(q_pos, kp, cu, hq, hkv))
+
+
+def test_bwd_plan_errors():
+    q_pos = np.arange(300, dtype=np.int32)
+    k_pos = np.arange(300, dtype=np.int32)
+    cu = np.array([0, 100, 300], np.int32)
+    lib = cp.load_library()
+    n = cp.cpattn_bwd_query_workgroups(300, 4)
+    assert n == 12
+    out = np.zeros(n + 1, np.int32)
+    st = lib.cpattn_varlen_bwd_plan(q_pos.ctypes.data, 300, k_pos.ctypes.data, 300, cu.ctypes.data, 2, 4, 4,
+                                    out.ctypes.data, n + 1)
+    assert st == 2  # CPATTN_ERR_SHAPE: plan_len is not the query kernel's workgroups
+    with pytest.raises(cp.CpattnError) as e:
+        cp.cpattn_varlen_bwd_plan(q_pos, k_pos[::-1].copy(), cu, 4, 4)
+    assert e.value.status == 4  # CPATTN_ERR_UNSORTED
+    with pytest.raises(cp.CpattnError) as e:
+        cp.cpattn_varlen_bwd_plan(q_pos, k_pos, cu, 6, 4)
+    assert e.value.status == 2
+    assert cp.cpattn_bwd_query_workgroups(-1, 4) == -1
+    assert cp.cpattn_bwd_query_workgroups(0, 4) == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["docs8k_zigzag_cp4_h2_d128", "docs8k_zigzag_cp4_h4kv2_d64"])
+def test_planned_gradients_bit_identical(name):
+    """The share's backward plans, a random order and the unplanned calls give
+    bit-identical dq, dk and dv."""
+    import torch
+    from test_backward import _reduced
+    from test_gpu_parity import say
+    from context_long_sequence_amd.share import bits_to_device, share_from_workload
+    wl = _reduced()[name]
+    say("%s: planned / random order / unplanned gradients" % name)
+    share = share_from_workload(wl)
+    assert share.bwd_plans is not None
+    order = list(wl.arrival())
+    share.step(order)
+    dout = bits_to_device(wl.dout())
+    res = []
+    dq, dk, dv = share.backward(dout, order)
+    res.append((dq.clone(), [x.clone() for x in dk], [x.clone() for x in dv]))
+    rng = np.random.default_rng(5)
+    share.bwd_plans = [pl[torch.from_numpy(rng.permutation(pl.numel())).cuda()].contiguous() for pl in share.bwd_plans]
+    dq, dk, dv = share.backward(dout, order)
+    res.append((dq.clone(), [x.clone() for x in dk], [x.clone() for x in dv]))
+    share.bwd_plans = None
+    dq, dk, dv = share.backward(dout, order)
+    res.append((dq.clone(), [x.clone() for x in dk], [x.clone() for x in dv]))
+    torch.cuda.synchronize()
+    for other in res[1:]:
+        assert torch.equal(res[0][0], other[0])
+        assert all(torch.equal(a, b) for a, b in zip(res[0][1], other[1]))
+        assert all(torch.equal(a, b) for a, b in zip(res[0][2], other[2]))

@@ -1,8 +1,8 @@
 """CPATTN_VALIDATE=1: the calls (the multi-block gradient call per block)
 copy the position arrays to the host and reject ones that do not ascend
-(CPATTN_ERR_UNSORTED), and a planned document call
-recomputes its plan and rejects one made for other positions
-(CPATTN_ERR_RANGE), before anything is enqueued.
+(CPATTN_ERR_UNSORTED), and a planned document call (forward or gradient)
+recomputes its plan and rejects a different one (CPATTN_ERR_RANGE), before
+anything is enqueued.
 The setting is read once per process, so the checks run in a child process
 started with it set."""
 import os
@@ -63,6 +63,13 @@ print("bwd sorted", status(lambda: cp.cpattn_partial_bwd(q, k, v, q, qp, kp, lse
 print("bwd k unsorted", status(lambda: cp.cpattn_partial_bwd(q, k, v, q, qp, bad_k, lse, delta, dq, dk, dv)))
 print("bwd cu unsorted", status(lambda: cp.cpattn_partial_bwd(q, k, v, q, qp, kp, lse, delta, dq, dk, dv,
                                                               cu_seqlens=bad_cu)))
+bplan = cp.cpattn_varlen_bwd_plan(qp.cpu().numpy(), kp.cpu().numpy(), cu.cpu().numpy(), hq, hq)
+bother = torch.from_numpy(bplan[::-1].copy()).to(dev)
+bplan = torch.from_numpy(bplan).to(dev)
+print("bwd plan", status(lambda: cp.cpattn_partial_bwd(q, k, v, q, qp, kp, lse, delta, dq, dk, dv, cu_seqlens=cu,
+                                                       plan=bplan)))
+print("bwd other plan", status(lambda: cp.cpattn_partial_bwd(q, k, v, q, qp, kp, lse, delta, dq, dk, dv,
+                                                             cu_seqlens=cu, plan=bother)))
 dk2, dv2 = torch.empty_like(dk), torch.empty_like(dv)
 print("bwd multi sorted", status(lambda: cp.cpattn_partial_bwd_multi(q, [k, k], [v, v], q, qp, [kp, kp], lse, delta,
                                                                      dq, [dk, dk2], [dv, dv2])))
@@ -92,6 +99,8 @@ def test_validate_rejects_unsorted_positions():
         "bwd sorted": "OK",
         "bwd k unsorted": "ERR_UNSORTED",
         "bwd cu unsorted": "ERR_UNSORTED",
+        "bwd plan": "OK",
+        "bwd other plan": "ERR_RANGE",
         "bwd multi sorted": "OK",
         "bwd multi k unsorted": "ERR_UNSORTED",
     }, got
