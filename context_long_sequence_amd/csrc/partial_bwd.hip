@@ -45,6 +45,9 @@
 //    one XCD (shared L2) when the heads split evenly over the 8 XCDs (else
 //    the hardware's round-robin order spreads the heavy tiles); the tiles
 //    with the most work go first.
+//  * With documents a query tile's work follows its rows' places in their
+//    documents, not their positions: a planned call takes the query kernel's
+//    order from a host plan (each XCD's tiles, most key tiles first).
 //  * Several blocks present at once (MULTI): the key kernel's grid covers
 //    every block's workgroups (a workgroup finds its block in a table of
 //    running workgroup counts, then runs the per-block code unchanged), and
