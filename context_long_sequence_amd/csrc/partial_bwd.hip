@@ -499,10 +499,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p, Bw
           dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m % RING], __builtin_bit_cast(bf16x8_t, hf ? bp1 : bp0),
                                                                dv_acc[dt], 0, 0, 0);
         if (m + RING < NM) a[m % RING] = rd(m + RING);
+        // the commit of tile k + 2 into stage (k + 2) % 4 (read by nobody since
+        // tile k - 2 left it) halfway through the products, so that its LDS
+        // writes run under the rest of them and the phase barrier has little to
+        // drain; its loads were issued a phase earlier
+        if (m == NM / 2 && k + 2 < n_it) commit((st + 3) & (NS - 1), cs);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (k + 2 < n_it) commit((st + 3) & (NS - 1), cs);  // stage (k + 2) % 4; st is (k - 1) % 4
+    if (k == 0 && k + 2 < n_it) commit((st + 3) & (NS - 1), cs);  // phase 0 has no products; st is (k - 1) % 4
     phase_barrier();
     st = (st + 1) & (NS - 1);
   };
