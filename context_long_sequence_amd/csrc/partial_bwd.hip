@@ -428,28 +428,43 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams p, Bw
           if (full) softmax_rr(s_c, dp_c, rr, std::false_type{});
           else softmax_rr(s_c, dp_c, rr, std::true_type{});
         };
+        // P, dS go to the stage the consumers read next phase (this phase's
+        // consumers read the other one): rows 0-15 (slices 0, 1) and 16-31
+        // (slices 2, 3), each half a 16-byte piece of P and one of dS per lane
+        char CPATTN_LDS* xb = (char CPATTN_LDS*)x_s[k & 1][kw] + 16 * lane;
+        auto put = [&](int h) __attribute__((always_inline)) {
+          *(u32x4 CPATTN_LDS*)(xb + 1024 * h) = u32x4{pp[4 * h], pp[4 * h + 1], pp[4 * h + 2], pp[4 * h + 3]};
+          *(u32x4 CPATTN_LDS*)(xb + 2048 + 1024 * h) =
+              u32x4{pd[4 * h], pd[4 * h + 1], pd[4 * h + 2], pd[4 * h + 3]};
+        };
+        // At d 128 the first half is written as soon as slice 1 has formed it,
+        // under the rest of the products (measured faster there; at d 64, with
+        // half the products per phase, slower)
+        constexpr bool kEarlyHalf = D == 128;
         if (k + 1 < n_it) {
           constexpr int SP = NQ / 2;  // MFMAs per slice
           static_assert(SP >= 2, "a slice's row reads go one MFMA ahead of it");
           f32x16_t s_n, dp_n;
           sdp(st1, s_n, dp_n, [&](int m) __attribute__((always_inline)) {
             if (m % SP == SP - 2) read_rows(st, m / SP);
-            if (m % SP == SP - 1) soft(m / SP);
+            if (m % SP == SP - 1) {
+              soft(m / SP);
+              if (kEarlyHalf && m / SP == 1) put(0);
+            }
           });
           s_c = s_n;
           dp_c = dp_n;
+          if (!kEarlyHalf) put(0);
+          put(1);
         } else {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             read_rows(st, rr);
             soft(rr);
           }
+          put(0);
+          put(1);
         }
-        char CPATTN_LDS* xb = (char CPATTN_LDS*)x_s[k & 1][kw] + 16 * lane;
-        *(u32x4 CPATTN_LDS*)(xb) = u32x4{pp[0], pp[1], pp[2], pp[3]};
-        *(u32x4 CPATTN_LDS*)(xb + 1024) = u32x4{pp[4], pp[5], pp[6], pp[7]};
-        *(u32x4 CPATTN_LDS*)(xb + 2048) = u32x4{pd[0], pd[1], pd[2], pd[3]};
-        *(u32x4 CPATTN_LDS*)(xb + 3072) = u32x4{pd[4], pd[5], pd[6], pd[7]};
       }
       phase_barrier();
       st = (st + 1) & (NS - 1);
